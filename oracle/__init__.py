@@ -1,0 +1,117 @@
+"""KDA oracle: float64 CPU token-by-token recurrence (ctypes wrapper over kda_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library and never imports it.
+
+The recurrence (see the header of ``kda_oracle.c`` for the page citations):
+
+    S' = Diag(exp(clamp(log_alpha_t, -5, 0))) S
+    e  = v_t - S'^T k_t
+    S  = S' + beta_t k_t e^T
+    o_t = S^T q_t
+
+Inputs are widened to float64 before the call, so the oracle sees exactly the
+values (bf16 or fp32) that a device path receives.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.kda_oracle_prefill.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                           ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                           ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                           ctypes.c_int]
+        lib.kda_oracle_prefill.restype = ctypes.c_int
+        lib.kda_oracle_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    if hasattr(x, "detach"):  # a torch tensor: widen on the host
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def prefill(q, k, v, log_alpha, beta, S0=None, nthreads: int | None = None,
+            col_block: int = 32):
+    """Run the recurrence over a whole batch.
+
+    q, k, log_alpha: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H];
+    S0: [B, H, dk, dv] or None.  Returns (o [B, T, H, dv], S_T [B, H, dk, dv]),
+    both float64 numpy arrays.
+    """
+    q, k, v, la, bt = (_f64(x) for x in (q, k, v, log_alpha, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or la.shape != q.shape:
+        raise ValueError("q, k and log_alpha must share the shape [B, T, H, dk]")
+    if v.shape[:3] != (B, T, H) or bt.shape != (B, T, H):
+        raise ValueError("v must be [B, T, H, dv] and beta [B, T, H]")
+    s0 = None
+    if S0 is not None:
+        s0 = _f64(S0)
+        if s0.shape != (B, H, dk, dv):
+            raise ValueError("S0 must be [B, H, dk, dv]")
+    o = np.empty((B, T, H, dv), dtype=np.float64)
+    st = np.empty((B, H, dk, dv), dtype=np.float64)
+    rc = _load().kda_oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bt), _ptr(s0),
+                                    _ptr(o), _ptr(st), B, T, H, dk, dv, col_block,
+                                    nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_prefill failed with code {rc}")
+    return o, st
+
+
+def decode_step(q, k, v, log_alpha, beta, S, nthreads: int | None = None):
+    """One decode step: exactly one token of the recurrence with S in and out.
+
+    q, k, log_alpha: [N, H, dk]; v: [N, H, dv]; beta: [N, H]; S: [N, H, dk, dv].
+    Returns (o [N, H, dv], S_new [N, H, dk, dv]) as float64 numpy arrays.
+    """
+    q, k, v, la, bt, s = (_f64(x) for x in (q, k, v, log_alpha, beta, S))
+    o, st = prefill(q[:, None], k[:, None], v[:, None], la[:, None], bt[:, None], s,
+                    nthreads=nthreads)
+    return o[:, 0], st
