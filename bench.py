@@ -1,0 +1,247 @@
+"""KDA benchmark on one MI355X: prefill tokens/s (+ decode state GB/s).
+
+One step = one chunked KDA prefill over the model-width batch (B=4, H=56,
+T=32768, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 log_alpha/beta/state) with
+all inputs already resident in HBM.  The same run also measures
+  * the decode step (256 sequences x 56 heads, fp32 state read-modify-written
+    in place, 1000 consecutive steps), reported as achieved state GB/s;
+  * the 1M-token prefill (B=1, H=16, T=1,048,576) split into 64K-token
+    segments (transitions + increments, on-device prefix scan, rerun);
+  * the float64 oracle on the host cores, on a bounded sample of the prefill
+    workload (the CPU baseline).
+Prints one JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s/GPU (H=56,d=128,bf16) + decode state GB/s vs HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published
+
+# Algorithmic work per token-head at d_k = d_v = 128, chunk 64 (bf16 q/k/v/o, fp32 log_alpha,
+# fp32 beta): bytes = q 256 + k 256 + v 256 + log_alpha 512 + beta 4 + o 256 = 1540.
+BYTES_PER_TOKEN_HEAD = 1540
+# Useful multiply-adds per token-head: five lower-triangular 16-token-tile products
+# (5 * (n+1)/2 * 16 * d with n = 4) + three state products (3 d^2) + the inverse (~1067).
+FLOPS_PER_TOKEN_HEAD = 2 * (5 * 2.5 * 16 * 128 + 3 * 128 * 128 + 1067)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_bytes(B, T, H, d, with_state=True):
+    b = B * T * H * BYTES_PER_TOKEN_HEAD
+    if with_state:
+        b += 2 * B * H * d * d * 4       # S0 read + S_T write
+    return b
+
+
+def decode_bytes(N, H, d):
+    state = N * H * d * d * 4
+    per_tok = N * H * (3 * d * 2 + d * 4 + 4 + d * 2)   # q, k, v bf16; log_alpha; beta; o bf16
+    return 2 * state + per_tok
+
+
+def time_loop(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, ev0.elapsed_time(ev1) / 1000.0
+
+
+def bench_prefill(kda, gen, steps, warmup):
+    import torch
+    w = gen.WORKLOADS["model_width"]
+    log(f"[prefill] generating {w.note} on the device")
+    d = gen.workload_inputs(w, device="cuda")
+    o = torch.empty_like(d["v"])
+    st = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
+                          chunk=w.chunk, o=o, S_T=st)
+
+    wall, ev = time_loop(step, steps, warmup, stream)
+    assert torch.isfinite(o[:, -64:].float()).all() and torch.isfinite(st).all()
+    plan = kda.prefill_plan(w.B, w.T, w.H, w.dk, w.dv, w.chunk)
+    log(f"[prefill] {steps} steps: wall {wall*1e3:.2f} ms, events {ev*1e3:.2f} ms, plan {plan}")
+    return w, d, wall, ev, plan
+
+
+def bench_long(kda, gen, steps, warmup):
+    import torch
+    w = gen.WORKLOADS["long_1m"]
+    log(f"[long] generating {w.note} on the device")
+    d = gen.workload_inputs(w, device="cuda")
+    o = torch.empty_like(d["v"])
+    st = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    need = kda.prefill_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.chunk, seg_len=w.segment)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
+                          chunk=w.chunk, seg_len=w.segment, o=o, S_T=st, workspace=ws)
+
+    wall, ev = time_loop(step, steps, warmup, stream)
+    assert torch.isfinite(st).all()
+    log(f"[long] {steps} steps: wall {wall*1e3:.2f} ms, events {ev*1e3:.2f} ms")
+    del d, o, ws
+    torch.cuda.empty_cache()
+    return w, wall, ev
+
+
+def bench_decode(kda, gen, steps=1000, pool=8):
+    import torch
+    w = gen.DECODE_WORKLOADS["decode_n256"]
+    log(f"[decode] {w.note}: state {w.N*w.H*w.dk*w.dv*4/1e9:.3f} GB, {pool} distinct token sets")
+    S = gen.make_state(w.N, w.H, w.dk, w.dv, w.s0_std, seed=w.seed, device="cuda")
+    toks = [gen.make_decode_inputs(w.N, w.H, w.dk, w.dv, w.dtype, w.decay, seed=w.seed * 10**6 + i,
+                                   device="cuda") for i in range(pool)]
+    o = torch.empty((w.N, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    it = [0]
+
+    def step():
+        t = toks[it[0] % pool]
+        it[0] += 1
+        kda.decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], S, o=o)
+
+    wall, ev = time_loop(step, steps, 10, stream)
+    assert torch.isfinite(S).all()
+    log(f"[decode] {steps} steps: wall {wall*1e3:.2f} ms, events {ev*1e3:.2f} ms")
+    return w, wall, ev
+
+
+def cpu_baseline(gen_inputs, w, budget_s=20.0):
+    """Oracle (float64, OpenMP) on the host cores over (b=0, first Hs heads, all T tokens)."""
+    import oracle
+    import torch
+    cores = oracle.default_threads()
+    sl = lambda x: x[0:1, :, :hs].contiguous().cpu()  # noqa: E731
+    hs = 1
+    t0 = time.perf_counter()
+    oracle.prefill(*(sl(gen_inputs[k]) for k in ("q", "k", "v", "log_alpha", "beta")),
+                   S0=gen_inputs["S0"][0:1, :hs].cpu(), nthreads=cores)
+    t1 = time.perf_counter() - t0
+    # the oracle parallelises over (head, 32-column block): 4 units per head at d_v = 128
+    hs = int(max(1, min(w.H, (budget_s / max(t1, 1e-3)) * max(1, cores // 4))))
+    hs = max(1, min(w.H, hs))
+    args = [sl(gen_inputs[k]) for k in ("q", "k", "v", "log_alpha", "beta")]
+    s0 = gen_inputs["S0"][0:1, :hs].cpu()
+    t0 = time.perf_counter()
+    oracle.prefill(*args, S0=s0, nthreads=cores)
+    el = time.perf_counter() - t0
+    token_heads = w.T * hs
+    tok_s = token_heads / w.H / el
+    log(f"[cpu] oracle on {hs} heads x {w.T} tokens: {el:.2f} s with {cores} threads")
+    del args, s0
+    return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"sequence 0, heads 0..{hs-1} of {w.H}, all {w.T} tokens "
+                      f"({token_heads} token-heads, {el:.1f} s); tokens/s = token-heads/s / {w.H}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_gated_delta_13_amd as kda
+    from chunked_gated_delta_13_amd import inputs as gen
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    kda.load_library()
+    torch.cuda.set_device(0)
+
+    w, d, wall, ev, plan = bench_prefill(kda, gen, args.steps, args.warmup)
+    tokens = w.B * w.T
+    tok_s = tokens * args.steps / wall
+    launch_s = ev / args.steps                 # one kernel launch per step (no split)
+    alg_bytes = prefill_bytes(w.B, w.T, w.H, w.dk)
+    achieved = alg_bytes / launch_s / 1e9
+    useful_tflops = FLOPS_PER_TOKEN_HEAD * w.B * w.T * w.H / launch_s / 1e12
+    result = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "KDA chunked prefill B4 H56 T32768 d128 chunk64 bf16 (7168 hidden)",
+                   "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
+                   "tokens_per_step": tokens, "seg_len": plan[0], "n_vs": plan[1],
+                   "parallelism": "1 GPU"},
+        "roofline": {"bound": "hbm", "kernel": "kda_prefill_kernel<128,2,64,bf16>",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": alg_bytes, "launch_ms": launch_s * 1e3,
+                     "useful_tflops": useful_tflops,
+                     "useful_frac_of_bf16_peak": useful_tflops / BF16_PEAK_TFLOPS},
+    }
+    if not args.prefill_only and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d, w)
+    del d
+    torch.cuda.empty_cache()
+
+    if not args.prefill_only and not args.no_decode:
+        wd, dwall, dev_s = bench_decode(kda, gen, args.decode_steps)
+        step_s = dev_s / args.decode_steps
+        gbs = decode_bytes(wd.N, wd.H, wd.dk) / step_s / 1e9
+        result["decode"] = {"workload": wd.note, "steps": args.decode_steps,
+                            "us_per_step": step_s * 1e6, "state_GBps": gbs,
+                            "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+                            "alg_bytes_per_step": decode_bytes(wd.N, wd.H, wd.dk),
+                            "tokens_per_s": wd.N * args.decode_steps / dwall}
+    if not args.prefill_only and not args.no_long:
+        wl, lwall, lev = bench_long(kda, gen, max(2, args.steps // 5), 1)
+        nsteps = max(2, args.steps // 5)
+        result["long_context"] = {"workload": wl.note, "seg_len": wl.segment, "steps": nsteps,
+                                  "ms_per_step": lwall / nsteps * 1e3,
+                                  "tokens_per_s": wl.B * wl.T * nsteps / lwall}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

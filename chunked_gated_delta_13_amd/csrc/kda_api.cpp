@@ -1,0 +1,368 @@
+// Host side of libkda: argument validation, the sequence-split planner and
+// kernel launches on the caller's stream.  Nothing here allocates memory or
+// synchronises the host with the device.
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace kda {
+hipError_t launch_prefill_bf16(int dk, int nct, int chunk, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(int dk, int nct, int chunk, const PrefillArgs& a, hipStream_t s);
+}  // namespace kda
+
+namespace {
+
+using kda::PrefillArgs;
+
+constexpr long long kMinSegTokens = 4096;   // shortest segment worth a transition pass
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+bool mul_ok(long long a, long long b, long long* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > (1LL << 62) / a) return false;
+    *out = a * b;
+    return true;
+}
+
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Shape checks shared by the prefill entry points.
+kda_status_t check_prefill_shape(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt) {
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_INVALID_ARGUMENT;
+    if (dk <= 0 || dv <= 0 || chunk <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (!kda::prefill_supported(dk, 1, chunk, dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
+    long long n = 0;
+    if (!mul_ok((long long)B * T, (long long)H * dk, &n)) return KDA_ERR_INVALID_ARGUMENT;
+    return KDA_OK;
+}
+
+// The automatic plan: column slices first (no extra work beyond the shared
+// per-chunk tiles), then segments when even that leaves most compute units idle.
+void auto_plan(int B, int T, int H, int dv, int chunk, int* seg_len, int* n_vs) {
+    const long long cus = cu_count();
+    const long long bh = (long long)B * H;
+    int vs = (dv == 128 && 2 * bh <= cus) ? 2 : 1;
+    long long seg = T;
+    const long long units = bh * vs;
+    if (units > 0 && 2 * units <= cus && (long long)T >= 2 * kMinSegTokens) {
+        long long nseg = cus / units;
+        if (nseg > T / kMinSegTokens) nseg = T / kMinSegTokens;
+        if (nseg >= 2) {
+            seg = ((long long)T + nseg - 1) / nseg;
+            seg = (seg + chunk - 1) / chunk * chunk;
+        }
+    }
+    if (seg_len) *seg_len = (int)(seg > 0 ? seg : chunk);
+    if (n_vs) *n_vs = vs;
+}
+
+// Resolve an explicit or automatic plan.  n_seg == 1 means no split.
+kda_status_t resolve_plan(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt,
+                          int seg_len_in, int n_vs_in, long long* seg_len, int* n_seg, int* n_vs) {
+    int a_seg = 0, a_vs = 0;
+    auto_plan(B, T, H, dv, chunk, &a_seg, &a_vs);
+    long long sl = seg_len_in > 0 ? seg_len_in : a_seg;
+    if (seg_len_in < 0 || (seg_len_in > 0 && seg_len_in % chunk != 0)) return KDA_ERR_INVALID_ARGUMENT;
+    int vs = n_vs_in > 0 ? n_vs_in : a_vs;
+    if (n_vs_in < 0 || vs > 2 || (vs == 2 && dv != 128)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!kda::prefill_supported(dk, (dv / vs) / 64, chunk, dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
+    if (sl <= 0 || sl >= T) sl = T > 0 ? T : chunk;
+    long long ns = T > 0 ? ((long long)T + sl - 1) / sl : 1;
+    if (ns > (1 << 20)) return KDA_ERR_UNSUPPORTED;
+    *seg_len = sl;
+    *n_seg = (int)ns;
+    *n_vs = vs;
+    return KDA_OK;
+}
+
+size_t workspace_for(int B, int H, int dk, int dv, int n_seg) {
+    if (n_seg <= 1) return 0;
+    const size_t bh = (size_t)B * H;
+    const size_t mats = (size_t)(n_seg - 1) * ((size_t)dk * dk + (size_t)dk * dv) + (size_t)n_seg * dk * dv;
+    return bh * mats * sizeof(float);
+}
+
+}  // namespace
+
+namespace kda {
+
+
+bool prefill_supported(int dk, int nct, int chunk, bool f32) {
+    if (nct != 1 && nct != 2) return false;
+    if (nct == 2 && dk != 128) return false;
+    if (dk != 64 && dk != 128) return false;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return false;
+    if (f32 && chunk == 64) return false;   // fp32 operands for a 64-token chunk exceed 160 KiB of LDS
+    return true;
+}
+
+hipError_t launch_prefill(int dk, int nct, int chunk, bool f32, const PrefillArgs& a, hipStream_t s) {
+    if (!prefill_supported(dk, nct, chunk, f32)) return hipErrorInvalidValue;
+    return f32 ? launch_prefill_f32(dk, nct, chunk, a, s) : launch_prefill_bf16(dk, nct, chunk, a, s);
+}
+
+}  // namespace kda
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT: bad shape, NULL pointer, misalignment or overlap";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head size, chunk or dtype not implemented";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_DEVICE: return "KDA_ERR_DEVICE: HIP runtime call or kernel launch failed";
+    }
+    return "KDA: unknown status";
+}
+
+kda_status_t kda_chunk_prefill_plan(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt,
+                                    int* seg_len, int* n_vs) {
+    const kda_status_t st = check_prefill_shape(B, T, H, dk, dv, chunk, dt);
+    if (st != KDA_OK) return st;
+    long long sl = 0;
+    int ns = 0, vs = 0;
+    const kda_status_t st2 = resolve_plan(B, T, H, dk, dv, chunk, dt, 0, 0, &sl, &ns, &vs);
+    if (st2 != KDA_OK) return st2;
+    if (seg_len) *seg_len = (int)sl;
+    if (n_vs) *n_vs = vs;
+    return KDA_OK;
+}
+
+size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt,
+                                         int seg_len) {
+    if (check_prefill_shape(B, T, H, dk, dv, chunk, dt) != KDA_OK) return 0;
+    long long sl = 0;
+    int ns = 0, vs = 0;
+    if (resolve_plan(B, T, H, dk, dv, chunk, dt, seg_len, 0, &sl, &ns, &vs) != KDA_OK) return 0;
+    return workspace_for(B, H, dk, dv, ns);
+}
+
+kda_status_t kda_chunk_prefill_ex(const void* q, const void* k, const void* v, const float* log_alpha,
+                                  const float* beta, const float* S0, void* o, float* S_T, int B, int T,
+                                  int H, int dk, int dv, int chunk, kda_dtype_t dt, int seg_len, int n_vs,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status_t st = check_prefill_shape(B, T, H, dk, dv, chunk, dt);
+    if (st != KDA_OK) return st;
+    long long sl = 0;
+    int ns = 0, vs = 0;
+    st = resolve_plan(B, T, H, dk, dv, chunk, dt, seg_len, n_vs, &sl, &ns, &vs);
+    if (st != KDA_OK) return st;
+    if (B == 0 || H == 0) return KDA_OK;
+
+    const size_t esz = dt == KDA_BF16 ? 2 : 4;
+    const size_t ntok = (size_t)B * T * H;
+    const size_t state_bytes = (size_t)B * H * dk * dv * sizeof(float);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    // pointers, alignment, aliasing
+    if (S0 && !aligned(S0, 16)) return KDA_ERR_INVALID_ARGUMENT;
+    if (S_T && !aligned(S_T, 16)) return KDA_ERR_INVALID_ARGUMENT;
+    if (S0 && S_T && S0 != S_T && overlap(range_of(S0, state_bytes), range_of(S_T, state_bytes)))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (T > 0) {
+        if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+            !aligned(log_alpha, 16) || !aligned(beta, 4))
+            return KDA_ERR_INVALID_ARGUMENT;
+        const Range ins[] = {range_of(q, ntok * dk * esz), range_of(k, ntok * dk * esz),
+                             range_of(v, ntok * dv * esz), range_of(log_alpha, ntok * dk * sizeof(float)),
+                             range_of(beta, ntok * sizeof(float))};
+        const Range ro = range_of(o, ntok * dv * esz);
+        for (const Range& r : ins) {
+            if (overlap(ro, r)) return KDA_ERR_INVALID_ARGUMENT;
+            if (S_T && overlap(range_of(S_T, state_bytes), r)) return KDA_ERR_INVALID_ARGUMENT;
+        }
+        if (S0 && overlap(ro, range_of(S0, state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
+        if (S_T && overlap(ro, range_of(S_T, state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    const size_t need = workspace_for(B, H, dk, dv, ns);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return KDA_ERR_WORKSPACE;
+        const Range rw = range_of(workspace, need);
+        if (overlap(rw, range_of(o, ntok * dv * esz))) return KDA_ERR_INVALID_ARGUMENT;
+        if (S_T && overlap(rw, range_of(S_T, state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
+        if (S0 && overlap(rw, range_of(S0, state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
+    }
+
+    (void)hipGetLastError();  // clear a stale error so a failure below is ours
+    if (T == 0) {
+        if (S_T && S_T != S0) {
+            if (kda::launch_state_copy(S_T, S0, (long long)B * H * dk * dv, s) != hipSuccess)
+                return KDA_ERR_DEVICE;
+        }
+        return KDA_OK;
+    }
+
+    const int nct = (dv / vs) / 64;
+    const bool f32 = dt == KDA_F32;
+    const long long SS = (long long)dk * dv;
+
+    PrefillArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.beta = beta;
+    a.T = T;
+    a.B = B;
+    a.H = H;
+    a.seg_len = sl;
+    a.n_vs = vs;
+
+    if (ns == 1) {
+        a.o = o;
+        a.s_in = S0;
+        a.sin_bh_stride = SS;
+        a.sin_seg_stride = 0;
+        a.init_mode = S0 ? 1 : 0;
+        a.s_out = S_T;
+        a.sout_bh_stride = SS;
+        a.sout_seg_stride = 0;
+        a.out_seg = -1;
+        a.seg0 = 0;
+        a.n_seg_launch = 1;
+        a.n_units = B * H;
+        a.zero_values = 0;
+        if (kda::launch_prefill(dk, nct, chunk, f32, a, s) != hipSuccess) return KDA_ERR_DEVICE;
+        return KDA_OK;
+    }
+
+    // ---- sequence split: transitions and increments, scan, then every segment ----
+    float* ws = reinterpret_cast<float*>(workspace);
+    const long long bh = (long long)B * H;
+    float* wsM = ws;
+    float* wsH = wsM + bh * (ns - 1) * SS;
+    float* wsSin = wsH + bh * (ns - 1) * SS;
+
+    PrefillArgs pm = a;  // M_s: identity columns, zero values, no output
+    pm.o = nullptr;
+    pm.s_in = nullptr;
+    pm.init_mode = 2;
+    pm.zero_values = 1;
+    pm.s_out = wsM;
+    pm.sout_bh_stride = (long long)(ns - 1) * SS;
+    pm.sout_seg_stride = SS;
+    pm.out_seg = -1;
+    pm.seg0 = 0;
+    pm.n_seg_launch = ns - 1;
+    pm.n_units = (int)(bh * (ns - 1));
+    if (kda::launch_prefill(dk, nct, chunk, f32, pm, s) != hipSuccess) return KDA_ERR_DEVICE;
+
+    PrefillArgs ph = pm;  // H_s: zero start, real values, no output
+    ph.init_mode = 0;
+    ph.zero_values = 0;
+    ph.s_out = wsH;
+    if (kda::launch_prefill(dk, nct, chunk, f32, ph, s) != hipSuccess) return KDA_ERR_DEVICE;
+
+    kda::ScanArgs sa;
+    sa.M = wsM;
+    sa.Hinc = wsH;
+    sa.S0 = S0;
+    sa.S_in = wsSin;  // S0 is copied here first, so S_T may alias S0
+    sa.BH = (int)bh;
+    sa.n_seg = ns;
+    if (kda::launch_scan(dk, sa, s) != hipSuccess) return KDA_ERR_DEVICE;
+
+    PrefillArgs pf = a;  // every segment from its entry state, with outputs
+    pf.o = o;
+    pf.s_in = wsSin;
+    pf.sin_bh_stride = (long long)ns * SS;
+    pf.sin_seg_stride = SS;
+    pf.init_mode = 1;
+    pf.zero_values = 0;
+    pf.s_out = S_T;
+    pf.sout_bh_stride = SS;
+    pf.sout_seg_stride = 0;
+    pf.out_seg = ns - 1;
+    pf.seg0 = 0;
+    pf.n_seg_launch = ns;
+    pf.n_units = (int)(bh * ns);
+    if (kda::launch_prefill(dk, nct, chunk, f32, pf, s) != hipSuccess) return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const float* beta, const float* S0, void* o, float* S_T, int B, int T, int H,
+                               int dk, int dv, int chunk, kda_dtype_t dt, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return kda_chunk_prefill_ex(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk, dt, 0, 0,
+                                workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, float* S, void* o, int N, int H, int dk, int dv,
+                             kda_dtype_t dt, void* stream) {
+    if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_INVALID_ARGUMENT;
+    if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+    long long nh = 0;
+    if (!mul_ok(N, H, &nh)) return KDA_ERR_INVALID_ARGUMENT;
+    if (nh == 0) return KDA_OK;
+    if (!q || !k || !v || !log_alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(S, 16) ||
+        !aligned(log_alpha, 16) || !aligned(beta, 4))
+        return KDA_ERR_INVALID_ARGUMENT;
+    const size_t esz = dt == KDA_BF16 ? 2 : 4;
+    const Range ro = range_of(o, (size_t)nh * dv * esz);
+    const Range rs = range_of(S, (size_t)nh * dk * dv * sizeof(float));
+    const Range ins[] = {range_of(q, (size_t)nh * dk * esz), range_of(k, (size_t)nh * dk * esz),
+                         range_of(v, (size_t)nh * dv * esz), range_of(log_alpha, (size_t)nh * dk * sizeof(float)),
+                         range_of(beta, (size_t)nh * sizeof(float))};
+    for (const Range& r : ins)
+        if (overlap(ro, r) || overlap(rs, r)) return KDA_ERR_INVALID_ARGUMENT;
+    if (overlap(ro, rs)) return KDA_ERR_INVALID_ARGUMENT;
+
+    kda::DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.beta = beta;
+    a.S = S;
+    a.o = o;
+    a.NH = nh;
+    (void)hipGetLastError();
+    if (kda::launch_decode(dk, dt == KDA_F32, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Host <-> kernel interface inside libkda (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kda {
+
+// One launch of the fused chunk kernel over units (b, h, segment, column slice).
+struct PrefillArgs {
+    const void* q;            // [B, T, H, DK]   bf16 or fp32
+    const void* k;            // [B, T, H, DK]
+    const void* v;            // [B, T, H, DK]   (d_v == d_k)
+    const float* log_alpha;   // [B, T, H, DK]
+    const float* beta;        // [B, T, H]
+    void* o;                  // [B, T, H, DK] or nullptr (no output)
+
+    // initial state of a unit (b, h, s): s_in + bh * sin_bh_stride + s * sin_seg_stride
+    const float* s_in;
+    long long sin_bh_stride;
+    long long sin_seg_stride;
+    int init_mode;            // 0: zeros, 1: load from s_in, 2: identity columns
+
+    // final state of a unit, written when out_seg < 0 or s == out_seg
+    float* s_out;
+    long long sout_bh_stride;
+    long long sout_seg_stride;
+    int out_seg;
+
+    long long T;              // tokens per sequence
+    int B, H;
+    long long seg_len;        // tokens per segment
+    int seg0;                 // first segment index of this launch
+    int n_seg_launch;         // segments per (b, h) in this launch
+    int n_vs;                 // state-column slices per unit
+    int n_units;              // B * H * n_seg_launch
+    int zero_values;          // 1: treat v as zeros (transition pass)
+};
+
+struct ScanArgs {
+    const float* M;           // [B*H, n_seg-1, DK, DK]
+    const float* Hinc;        // [B*H, n_seg-1, DK, DK]
+    const float* S0;          // [B*H, DK, DK] or nullptr
+    float* S_in;              // [B*H, n_seg, DK, DK]  (out)
+    int BH;
+    int n_seg;
+};
+
+struct DecodeArgs {
+    const void* q;            // [NH, DK]
+    const void* k;
+    const void* v;            // [NH, DK]
+    const float* log_alpha;   // [NH, DK]
+    const float* beta;        // [NH]
+    float* S;                 // [NH, DK, DK]
+    void* o;                  // [NH, DK]
+    long long NH;
+};
+
+bool prefill_supported(int dk, int nct, int chunk, bool f32);
+hipError_t launch_prefill(int dk, int nct, int chunk, bool f32, const PrefillArgs& a,
+                          hipStream_t stream);
+hipError_t launch_scan(int dk, const ScanArgs& a, hipStream_t stream);
+hipError_t launch_decode(int dk, bool f32, const DecodeArgs& a, hipStream_t stream);
+// dst[i] = src ? src[i] : 0 for n floats
+hipError_t launch_state_copy(float* dst, const float* src, long long n, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,23 @@
+// fp32-input instantiations of the fused chunk-prefill kernel (fp32 matrix-core operands).
+#include "kda_prefill_kernel.h"
+
+namespace kda {
+
+hipError_t launch_prefill_f32(int dk, int nct, int chunk, const PrefillArgs& a, hipStream_t s) {
+    using T = float;
+    if (dk == 128 && nct == 2) {
+        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<128, 2, 32, T>>(a, s);
+        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<128, 2, 16, T>>(a, s);
+    }
+    if (dk == 128 && nct == 1) {
+        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<128, 1, 32, T>>(a, s);
+        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<128, 1, 16, T>>(a, s);
+    }
+    if (dk == 64 && nct == 1) {
+        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<64, 1, 32, T>>(a, s);
+        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<64, 1, 16, T>>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -1,0 +1,157 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) Kimi Delta Attention library (libkda.so).
+ *
+ * What is computed (per sequence b and head h; heads and sequences are
+ * independent).  Sources: "Inside Kimi K3: Architecture of an Open Frontier
+ * Model" (academa.ai lecture), sequence paragraph — a fixed-size state carried
+ * token to token, a diagonal forget gate alpha that shrinks retained history,
+ * a beta-scaled delta write that corrects what is stored, log-decay bounded
+ * below at -5; "Kimi K3" (meridianbulletin.com), "Handling One Million Tokens
+ * with a Fixed-Size State Matrix" (alpha clamped to [e^-5, 1]) and
+ * "Parallelizing Sequential State Updates" (tokens of a chunk in parallel,
+ * then state hand-off; a scheduler that spreads long prefill over the compute
+ * units of one card; transitions and increments joined by a prefix scan).
+ * The update formula is not printed on the pages; the reading used here, with
+ * S a d_k x d_v fp32 matrix whose rows are key channels, is
+ *
+ *     S <- Diag(exp(clamp(log_alpha_t, -5, 0))) S        forget
+ *     S <- S + beta_t k_t (v_t - S^T k_t)^T                delta write
+ *     o_t = S^T q_t                                        read after the write
+ *
+ * No scaling of q or k is applied inside the library; callers pass the
+ * (L2-normalised) vectors they want used.  log_alpha values outside [-5, 0]
+ * are clamped on load.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains them.  Scratch memory comes only from
+ *    the caller's `workspace`.
+ *  - Layouts are contiguous row-major.  Pointers must be 16-byte aligned
+ *    (beta: 4-byte aligned).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; no call synchronises the host with the device.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    rejected call returns an error status and enqueues nothing.  A launch
+ *    failure returns KDA_ERR_DEVICE.  Valid inputs produce no in-kernel errors.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* bad shape, NULL pointer, misalignment, overlap */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head size, chunk, dtype) */
+    KDA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+    KDA_ERR_DEVICE = 4            /* a HIP runtime call or kernel launch failed */
+} kda_status_t;
+
+/* Element type of q, k, v and o.  log_alpha, beta and the states are always fp32. */
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype_t;
+
+/* Returns KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kda_status_string(kda_status_t status);
+
+/*
+ * Sequence-split plan that kda_chunk_prefill picks for a shape (the automatic
+ * scheduler): `seg_len` tokens per segment (== T when the sequence is not
+ * split) and `n_vs` state-column slices per head.  Pages: "Kimi K3",
+ * "Parallelizing Sequential State Updates" (a scheduler spreads long-context
+ * prefill over the compute units of one card).  Any output pointer may be NULL.
+ */
+kda_status_t kda_chunk_prefill_plan(int B, int T, int H, int dk, int dv, int chunk,
+                                    kda_dtype_t dtype, int *seg_len, int *n_vs);
+
+/*
+ * Bytes of device workspace that kda_chunk_prefill_ex needs for `seg_len`
+ * (0 = the automatic plan).  0 when the sequence is not split.  Returns 0 for
+ * shapes that kda_chunk_prefill would reject.
+ */
+size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                         kda_dtype_t dtype, int seg_len);
+
+/*
+ * Chunked KDA prefill over T tokens from the initial state S0.
+ * Pages: "Kimi K3", "Parallelizing Sequential State Updates" (chunk-parallel
+ * tokens, state hand-off); "Kimi K3's architecture" (orkas.ai), "A lower bound
+ * that deleted a GPU code path" (bounded log-decay lets diagonal and
+ * off-diagonal 16-token tiles share one dense matrix product).
+ *
+ *   q, k       [B, T, H, dk]  dtype          queries, keys
+ *   v          [B, T, H, dv]  dtype          values
+ *   log_alpha  [B, T, H, dk]  fp32           per-channel log forget gate (clamped to [-5, 0])
+ *   beta       [B, T, H]      fp32           write strength
+ *   S0         [B, H, dk, dv] fp32 or NULL   initial state (NULL = zeros)
+ *   o          [B, T, H, dv]  dtype  (out)   outputs o_t = S_t^T q_t
+ *   S_T        [B, H, dk, dv] fp32 or NULL   final state (NULL = not written);
+ *                                            may be exactly S0 (in place), must not
+ *                                            partially overlap it
+ *   chunk      16, 32 or 64 tokens per chunk (64 only for KDA_BF16); the result
+ *              does not depend on it beyond rounding
+ *   dk == dv   64 or 128
+ *   workspace  device scratch of at least kda_chunk_prefill_workspace_bytes(...,0)
+ *              bytes (may be NULL when that is 0)
+ * T == 0 is valid: S_T receives S0 (or zeros).  B == 0 or H == 0 is a no-op.
+ */
+kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v,
+                               const float *log_alpha, const float *beta, const float *S0,
+                               void *o, float *S_T,
+                               int B, int T, int H, int dk, int dv, int chunk,
+                               kda_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
+ * kda_chunk_prefill with an explicit plan: `seg_len` tokens per segment (a
+ * positive multiple of `chunk`; 0 = automatic; >= T = no split) and `n_vs`
+ * state-column slices (1 or 2 for dv = 128, 1 for dv = 64; 0 = automatic).
+ * With a split, each segment's transition M_s (the recurrence applied to the
+ * identity with zero values) and increment H_s (from a zero state) are formed
+ * first, joined by an on-device prefix scan S_in(s+1) = M_s S_in(s) + H_s, and
+ * every segment is then run from its entry state.  Pages: "Kimi K3's
+ * architecture", "The bill comes due in the serving stack" (a segment is a
+ * cumulative transition plus a zero-start state, two quantities that compose).
+ * The workspace must hold kda_chunk_prefill_workspace_bytes(..., seg_len).
+ */
+kda_status_t kda_chunk_prefill_ex(const void *q, const void *k, const void *v,
+                                  const float *log_alpha, const float *beta, const float *S0,
+                                  void *o, float *S_T,
+                                  int B, int T, int H, int dk, int dv, int chunk,
+                                  kda_dtype_t dtype, int seg_len, int n_vs,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step for N independent sequences: exactly one token of the
+ * recurrence, with the state read and written in place.  Pages: "Inside Kimi
+ * K3", sequence paragraph (constant cost per new token); "Kimi K3's
+ * architecture", "The bill comes due in the serving stack" (the state updates
+ * in place).
+ *
+ *   q, k       [N, H, dk]      dtype
+ *   v          [N, H, dv]      dtype
+ *   log_alpha  [N, H, dk]      fp32   (clamped to [-5, 0])
+ *   beta       [N, H]          fp32
+ *   S          [N, H, dk, dv]  fp32   in/out, updated in place
+ *   o          [N, H, dv]      dtype  (out)
+ *   dk == dv   64 or 128
+ * N == 0 or H == 0 is a no-op.  o must not overlap any input or S.
+ */
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta, float *S, void *o,
+                             int N, int H, int dk, int dv, kda_dtype_t dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,193 @@
+"""C ABI of libkda.so on the host (no GPU needed, no kernel is ever launched).
+
+* the library loads and exports every function include/kda.h declares;
+* every validation branch returns its documented status before anything is
+  enqueued (fake, never-dereferenced pointer values are used, so these cases
+  are skipped where a GPU is present);
+* the planner and workspace sizing follow their stated rules;
+* the Python binding refuses host tensors and a missing library (no fallback).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import chunked_gated_delta_13_amd as kda
+from chunked_gated_delta_13_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+BF16, F32 = 0, 1
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+@pytest.fixture
+def host_only():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake pointers are only passed where no GPU exists")
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(kda_\w+)", out))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_abi_version() == 1
+    for code in range(5):
+        s = lib.kda_status_string(code).decode()
+        assert s.startswith("KDA_")
+    assert "unknown" in lib.kda_status_string(99).decode()
+
+
+def _prefill(lib, B=1, T=128, H=2, dk=128, dv=128, chunk=64, dt=BF16, seg=0, nvs=0,
+             q=0x10000, k=0x20000, v=0x30000, la=0x40000, beta=0x50000, S0=None, o=0x60000,
+             S_T=None, ws=None, ws_bytes=0):
+    vp = ctypes.c_void_p
+    return lib.kda_chunk_prefill_ex(vp(q), vp(k), vp(v), vp(la), vp(beta), vp(S0), vp(o),
+                                    vp(S_T), B, T, H, dk, dv, chunk, dt, seg, nvs, vp(ws),
+                                    ws_bytes, None)
+
+
+BIG = 1 << 40  # fake, well-separated, 16-byte-aligned addresses
+
+
+def _ptrs(i):
+    return BIG * (i + 1)
+
+
+def _ok_ptrs():
+    return dict(q=_ptrs(0), k=_ptrs(1), v=_ptrs(2), la=_ptrs(3), beta=_ptrs(4), o=_ptrs(5))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dk=96, dv=96), UNSUPPORTED),
+    (dict(dk=128, dv=64), UNSUPPORTED),
+    (dict(chunk=48), UNSUPPORTED),
+    (dict(chunk=64, dt=F32), UNSUPPORTED),
+    (dict(B=-1), INVALID),
+    (dict(T=-5), INVALID),
+    (dict(H=-2), INVALID),
+    (dict(dt=7), INVALID),
+    (dict(chunk=0), INVALID),
+    (dict(seg=100), INVALID),        # not a multiple of the chunk
+    (dict(seg=-64), INVALID),
+    (dict(nvs=3), INVALID),
+    (dict(dk=64, dv=64, nvs=2), INVALID),
+])
+def test_prefill_shape_validation(lib, kw, expect):
+    args = _ok_ptrs()
+    args.update(kw)
+    assert _prefill(lib, **args) == expect
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "la", "beta", "o"])
+def test_prefill_null_pointer(lib, host_only, field):
+    args = _ok_ptrs()
+    args[field] = None
+    assert _prefill(lib, **args) == INVALID
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "la", "o"])
+def test_prefill_misaligned_pointer(lib, host_only, field):
+    args = _ok_ptrs()
+    args[field] += 8
+    assert _prefill(lib, **args) == INVALID
+
+
+def test_prefill_overlaps(lib, host_only):
+    args = _ok_ptrs()
+    args["o"] = args["q"] + 64          # o overlaps q
+    assert _prefill(lib, **args) == INVALID
+    args = _ok_ptrs()
+    state = 2 * 128 * 128 * 4
+    assert _prefill(lib, S0=_ptrs(6), S_T=_ptrs(6) + state // 2, **args) == INVALID
+    assert _prefill(lib, S0=_ptrs(6), S_T=args["v"], **args) == INVALID   # S_T over an input
+
+
+def test_prefill_workspace_required(lib, host_only):
+    args = _ok_ptrs()
+    need = lib.kda_chunk_prefill_workspace_bytes(1, 8192, 2, 128, 128, 64, BF16, 2048)
+    assert need == 2 * (3 * 2 * 128 * 128 + 4 * 128 * 128) * 4
+    assert _prefill(lib, T=8192, seg=2048, **args) == WORKSPACE
+    assert _prefill(lib, T=8192, seg=2048, ws=_ptrs(7), ws_bytes=need - 4, **args) == WORKSPACE
+
+
+def test_prefill_empty_batch_is_noop(lib):
+    assert _prefill(lib, B=0, q=None, k=None, v=None, la=None, beta=None, o=None) == OK
+    assert _prefill(lib, H=0, q=None, k=None, v=None, la=None, beta=None, o=None) == OK
+
+
+def _decode(lib, N=2, H=3, dk=128, dv=128, dt=BF16, q=_ptrs(0), k=_ptrs(1), v=_ptrs(2),
+            la=_ptrs(3), beta=_ptrs(4), S=_ptrs(5), o=_ptrs(6)):
+    vp = ctypes.c_void_p
+    return lib.kda_decode_step(vp(q), vp(k), vp(v), vp(la), vp(beta), vp(S), vp(o), N, H, dk, dv,
+                               dt, None)
+
+
+def test_decode_validation(lib, host_only):
+    assert _decode(lib, dk=96, dv=96) == UNSUPPORTED
+    assert _decode(lib, N=-1) == INVALID
+    assert _decode(lib, dt=5) == INVALID
+    assert _decode(lib, q=None) == INVALID
+    assert _decode(lib, S=_ptrs(5) + 4) == INVALID
+    assert _decode(lib, o=_ptrs(5) + 256) == INVALID     # o inside S
+    assert _decode(lib, o=_ptrs(2)) == INVALID           # o over v
+    assert _decode(lib, N=0, q=None, k=None, v=None, la=None, beta=None, S=None, o=None) == OK
+
+
+def test_plan_rules(lib):
+    seg = ctypes.c_int(0)
+    nvs = ctypes.c_int(0)
+    # many heads: no split, one column slice per head
+    assert lib.kda_chunk_prefill_plan(4, 32768, 56, 128, 128, 64, BF16, ctypes.byref(seg),
+                                      ctypes.byref(nvs)) == OK
+    assert (seg.value, nvs.value) == (32768, 1)
+    # few heads, long sequence: column slices and segments
+    assert lib.kda_chunk_prefill_plan(1, 1 << 20, 16, 128, 128, 64, BF16, ctypes.byref(seg),
+                                      ctypes.byref(nvs)) == OK
+    assert nvs.value == 2 and seg.value % 64 == 0 and seg.value < (1 << 20)
+    # short sequence: never split below the minimum segment length
+    assert lib.kda_chunk_prefill_plan(1, 6000, 1, 128, 128, 64, BF16, ctypes.byref(seg),
+                                      ctypes.byref(nvs)) == OK
+    assert seg.value == 6000
+    assert lib.kda_chunk_prefill_workspace_bytes(1, 6000, 1, 128, 128, 64, BF16, 0) == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    la = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        kda.chunk_prefill(q, q, q, la, torch.zeros(1, 4, 1))
+    with pytest.raises(ValueError):
+        kda.decode_step(q[:, 0], q[:, 0], q[:, 0], la[:, 0], torch.zeros(1, 1),
+                        torch.zeros(1, 1, 64, 64))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load(str(tmp_path / "libkda.so"))

@@ -1,0 +1,251 @@
+"""Device path vs the float64 oracle, element by element, on seeded inputs.
+
+Sizes are small enough for the oracle to finish in seconds while spanning
+several chunks, several 16-token tiles and a ragged tail.  Every call goes
+through the C ABI of libkda.so (via the ctypes binding).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_gated_delta_13_amd import inputs as gen
+from tests.parity import assert_close, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _kda():
+    import chunked_gated_delta_13_amd as kda
+    kda.load_library()
+    return kda
+
+
+def _run_prefill(inp, chunk, seg_len=0, n_vs=0, inplace=False):
+    kda = _kda()
+    d = to_device(inp)
+    S0 = d["S0"]
+    kw = {}
+    if inplace:
+        assert S0 is not None
+        kw["S_T"] = S0
+    o, st = kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], S0, chunk=chunk,
+                              seg_len=seg_len, n_vs=n_vs, **kw)
+    torch.cuda.synchronize()
+    return o, st
+
+
+def _oracle(inp):
+    return oracle.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
+
+
+def _case(B, T, H, d, dtype, decay="sig2", s0=0.02, seed=0, bound_frac=0.0):
+    return gen.make_prefill_inputs(B, T, H, d, d, dtype, decay, s0, seed, bound_frac, "cpu")
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_step_matches_oracle(dtype, d):
+    kda = _kda()
+    print(f"decode dtype={dtype} d={d}", flush=True)
+    N, H = 5, 3
+    tok = gen.make_decode_inputs(N, H, d, d, dtype, "sig2", seed=11, device="cpu")
+    S = gen.make_state(N, H, d, d, 1.0, seed=12, device="cpu")
+    dv = to_device(tok)
+    Sd = S.cuda()
+    o = kda.decode_step(dv["q"], dv["k"], dv["v"], dv["log_alpha"], dv["beta"], Sd)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.decode_step(tok["q"], tok["k"], tok["v"], tok["log_alpha"], tok["beta"], S)
+    assert_close("o", o, o_ref, dtype)
+    assert_close("S", Sd, s_ref, dtype)
+
+
+def test_decode_many_steps_matches_oracle():
+    kda = _kda()
+    N, H, d, steps = 4, 3, 128, 40
+    S = gen.make_state(N, H, d, d, 0.02, seed=13, device="cpu")
+    Sd = S.cuda()
+    S_ref = to_f64(S)
+    for step in range(steps):
+        tok = gen.make_decode_inputs(N, H, d, d, "bf16", "sig2", seed=1000 + step, device="cpu")
+        dv = to_device(tok)
+        o = kda.decode_step(dv["q"], dv["k"], dv["v"], dv["log_alpha"], dv["beta"], Sd)
+        o_ref, S_ref = oracle.decode_step(tok["q"], tok["k"], tok["v"], tok["log_alpha"],
+                                          tok["beta"], S_ref)
+        torch.cuda.synchronize()
+        assert_close(f"o step {step}", o, o_ref, "bf16")
+    assert_close("S after steps", Sd, S_ref, "bf16")
+
+
+def test_decode_equals_prefill_of_one_token():
+    kda = _kda()
+    N, H, d = 3, 2, 128
+    inp = _case(N, 1, H, d, "bf16", s0=0.5, seed=14)
+    dv = to_device(inp)
+    S = dv["S0"].clone()
+    o_dec = kda.decode_step(dv["q"][:, 0].contiguous(), dv["k"][:, 0].contiguous(),
+                            dv["v"][:, 0].contiguous(), dv["log_alpha"][:, 0].contiguous(),
+                            dv["beta"][:, 0].contiguous(), S)
+    o_pf, st = kda.chunk_prefill(dv["q"], dv["k"], dv["v"], dv["log_alpha"], dv["beta"], dv["S0"],
+                                 chunk=16)
+    torch.cuda.synchronize()
+    assert_close("o", o_dec, o_pf[:, 0], "bf16")
+    assert_close("S", S, st, "bf16")
+
+
+# ----------------------------------------------------------------- prefill
+def test_prefill_tiny_fp32_workload():
+    """B1 H1 T256 d64, chunk 16, fp32 everywhere, S0 = 0, seed 0."""
+    w = gen.WORKLOADS["tiny_f32"]
+    inp = gen.workload_inputs(w)
+    o, st = _run_prefill(inp, w.chunk)
+    o_ref, s_ref = _oracle(inp)
+    assert_close("o", o, o_ref, "f32")
+    assert_close("S_T", st, s_ref, "f32")
+
+
+CASES = [
+    # (B, T, H, d, dtype, chunk)
+    (1, 200, 2, 64, "f32", 16),
+    (1, 200, 2, 64, "f32", 32),
+    (2, 77, 3, 128, "f32", 32),
+    (1, 300, 2, 128, "bf16", 64),
+    (2, 130, 3, 128, "bf16", 32),
+    (1, 250, 2, 128, "bf16", 16),
+    (2, 129, 2, 64, "bf16", 64),
+    (1, 1, 2, 128, "bf16", 64),
+    (1, 15, 1, 128, "bf16", 64),
+    (1, 33, 1, 64, "f32", 16),
+]
+
+
+@pytest.mark.parametrize("B,T,H,d,dtype,chunk", CASES)
+def test_prefill_matches_oracle(B, T, H, d, dtype, chunk):
+    print(f"prefill B={B} T={T} H={H} d={d} {dtype} chunk={chunk}", flush=True)
+    inp = _case(B, T, H, d, dtype, seed=T + d + chunk)
+    o, st = _run_prefill(inp, chunk)
+    o_ref, s_ref = _oracle(inp)
+    assert_close("o", o, o_ref, dtype)
+    assert_close("S_T", st, s_ref, dtype)
+
+
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("f32", 32)])
+def test_prefill_slow_decay_long_memory(dtype, chunk):
+    """log alpha ~ -0.05 sigmoid, S0 ~ N(0, 1): S0 and early chunks matter at the end."""
+    inp = _case(1, 1000, 2, 128, dtype, decay="slow", s0=1.0, seed=21)
+    o, st = _run_prefill(inp, chunk)
+    o_ref, s_ref = _oracle(inp)
+    assert_close("o", o, o_ref, dtype)
+    assert_close("S_T", st, s_ref, dtype)
+
+
+@pytest.mark.parametrize("fill", [-5.0, 0.0, -100.0])
+def test_prefill_decay_extremes(fill):
+    """All log alpha at the bound (tile reciprocal exactly e^80), at 0, or clamped from -100."""
+    inp = _case(1, 160, 2, 128, "bf16", s0=1.0, seed=22)
+    inp["log_alpha"] = torch.full_like(inp["log_alpha"], fill)
+    o, st = _run_prefill(inp, 64)
+    o_ref, s_ref = _oracle(inp)
+    assert_close("o", o, o_ref, "bf16")
+    assert_close("S_T", st, s_ref, "bf16")
+
+
+def test_prefill_mixed_bound_tokens():
+    inp = _case(1, 700, 2, 128, "bf16", decay="slow", s0=1.0, seed=23, bound_frac=0.1)
+    o, st = _run_prefill(inp, 64)
+    o_ref, s_ref = _oracle(inp)
+    assert_close("o", o, o_ref, "bf16")
+    assert_close("S_T", st, s_ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype,chunk,seg", [("bf16", 64, 256), ("bf16", 32, 192), ("f32", 16, 128)])
+def test_prefill_sequence_split_matches_oracle(dtype, chunk, seg):
+    """Transitions + increments per segment, prefix scan, rerun from entry states."""
+    inp = _case(2, 1000, 2, 128 if dtype == "bf16" else 64, dtype, decay="slow", s0=1.0, seed=24)
+    o, st = _run_prefill(inp, chunk, seg_len=seg)
+    o_ref, s_ref = _oracle(inp)
+    assert_close("o", o, o_ref, dtype)
+    assert_close("S_T", st, s_ref, dtype)
+
+
+def test_prefill_column_split_matches_unsplit():
+    inp = _case(1, 300, 3, 128, "bf16", seed=25)
+    o1, s1 = _run_prefill(inp, 64, n_vs=1)
+    o2, s2 = _run_prefill(inp, 64, n_vs=2)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_prefill_in_place_state():
+    inp = _case(2, 150, 2, 128, "bf16", s0=1.0, seed=26)
+    o_ref, s_ref = _oracle(inp)
+    o, st = _run_prefill(inp, 64, inplace=True)
+    assert_close("o", o, o_ref, "bf16")
+    assert_close("S_T", st, s_ref, "bf16")
+
+
+def test_prefill_in_place_state_with_split():
+    inp = _case(1, 600, 2, 128, "bf16", decay="slow", s0=1.0, seed=27)
+    o_ref, s_ref = _oracle(inp)
+    o, st = _run_prefill(inp, 64, seg_len=128, inplace=True)
+    assert_close("o", o, o_ref, "bf16")
+    assert_close("S_T", st, s_ref, "bf16")
+
+
+def test_prefill_zero_tokens_returns_initial_state():
+    kda = _kda()
+    inp = _case(2, 0, 3, 128, "bf16", s0=1.0, seed=28)
+    d = to_device(inp)
+    o, st = kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 3, 128)
+    assert torch.equal(st, d["S0"])
+    o, st = kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(st).item() == 0
+
+
+def test_prefill_zero_initial_state_is_default():
+    inp = _case(1, 100, 2, 128, "bf16", s0=0.0, seed=29)
+    assert inp["S0"] is None
+    o, st = _run_prefill(inp, 64)
+    o_ref, s_ref = _oracle(inp)
+    assert_close("o", o, o_ref, "bf16")
+    assert_close("S_T", st, s_ref, "bf16")
+
+
+def test_prefill_is_deterministic():
+    inp = _case(2, 500, 3, 128, "bf16", seed=30)
+    o1, s1 = _run_prefill(inp, 64)
+    o2, s2 = _run_prefill(inp, 64)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_prefill_chunk_size_independence_on_device():
+    inp = _case(1, 400, 2, 128, "bf16", decay="slow", s0=1.0, seed=31)
+    o_ref, s_ref = _oracle(inp)
+    for chunk in (16, 32, 64):
+        o, st = _run_prefill(inp, chunk)
+        assert_close(f"o chunk={chunk}", o, o_ref, "bf16")
+        assert_close(f"S_T chunk={chunk}", st, s_ref, "bf16")
+
+
+def test_prefill_small_bf16_workload():
+    """B1 H8 T4096 d128, chunk 64, bf16 q/k/v, fp32 beta / log alpha, S0 ~ N(0, 0.02)."""
+    w = gen.WORKLOADS["small_bf16"]
+    inp = gen.workload_inputs(w)
+    o, st = _run_prefill(inp, w.chunk)
+    o_ref, s_ref = _oracle(inp)
+    assert_close("o", o, o_ref, "bf16")
+    assert_close("S_T", st, s_ref, "bf16")
+
+
+def test_native_library_is_the_one_loaded():
+    kda = _kda()
+    lib = kda._lib.LIB_PATH
+    maps = open("/proc/self/maps").read()
+    assert lib in maps
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, f"more than one HIP runtime mapped: {hip}"
