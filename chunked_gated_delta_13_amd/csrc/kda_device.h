@@ -17,12 +17,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
+
+// LDS (address space 3) pointers keep shared-memory addressing in 32 bits.
+#define KDA_LDS __attribute__((address_space(3)))
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLogAlphaMin = -5.0f;  // bound on log alpha (natural log)
@@ -71,27 +78,94 @@ __device__ __forceinline__ f32x4_t mma(const Frag<float>& a, const Frag<float>& 
     return c;
 }
 
-// Load the eight slots of one row of a row-major LDS array: elements
-// p[kmap(g, 0..3)] and p[kmap(g, 4..7)] relative to the 32-block start.
-__device__ __forceinline__ void lds_row_frag(Frag<__bf16>& f, const __bf16* blk, int g) {
-    const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(blk + 4 * g);
-    const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(blk + 16 + 4 * g);
+// The eight slots of one lane from a row-major LDS array, `p` already pointing
+// at element kmap(g, 0) of the lane's row: p[0..3] and p[16..19].
+__device__ __forceinline__ void frag_ld(Frag<__bf16>& f, const KDA_LDS __bf16* p) {
+    const bf16x4_t lo = *reinterpret_cast<const KDA_LDS bf16x4_t*>(p);
+    const bf16x4_t hi = *reinterpret_cast<const KDA_LDS bf16x4_t*>(p + 16);
     f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-
-__device__ __forceinline__ void lds_row_frag(Frag<float>& f, const float* blk, int g) {
-    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(blk + 4 * g);
-    const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(blk + 16 + 4 * g);
+__device__ __forceinline__ void frag_ld(Frag<float>& f, const KDA_LDS float* p) {
+    const f32x4_t lo = *reinterpret_cast<const KDA_LDS f32x4_t*>(p);
+    const f32x4_t hi = *reinterpret_cast<const KDA_LDS f32x4_t*>(p + 16);
     f.v[0] = lo[0]; f.v[1] = lo[1]; f.v[2] = lo[2]; f.v[3] = lo[3];
     f.v[4] = hi[0]; f.v[5] = hi[1]; f.v[6] = hi[2]; f.v[7] = hi[3];
 }
 
-// Eight fp32 factors for the same slots (used for per-channel decay factors).
-__device__ __forceinline__ void lds_row_f32x8(float out[8], const float* blk, int g) {
-    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(blk + 4 * g);
-    const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(blk + 16 + 4 * g);
+// Only the lower four slots from LDS, the upper four zero: a 16-wide contraction block.
+__device__ __forceinline__ void frag_ld_lo(Frag<__bf16>& f, const KDA_LDS __bf16* p) {
+    const bf16x4_t lo = *reinterpret_cast<const KDA_LDS bf16x4_t*>(p);
+    const bf16x4_t z = {(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+    f.v = __builtin_shufflevector(lo, z, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void frag_ld_lo(Frag<float>& f, const KDA_LDS float* p) {
+    const f32x4_t lo = *reinterpret_cast<const KDA_LDS f32x4_t*>(p);
+    f.v[0] = lo[0]; f.v[1] = lo[1]; f.v[2] = lo[2]; f.v[3] = lo[3];
+    f.v[4] = 0.0f; f.v[5] = 0.0f; f.v[6] = 0.0f; f.v[7] = 0.0f;
+}
+
+// Eight fp32 factors for the same slots (per-channel decay factors).
+__device__ __forceinline__ void f32x8_ld(float out[8], const KDA_LDS float* p) {
+    const f32x4_t lo = *reinterpret_cast<const KDA_LDS f32x4_t*>(p);
+    const f32x4_t hi = *reinterpret_cast<const KDA_LDS f32x4_t*>(p + 16);
     out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
     out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane i of the wave writes
+// bytes [16 i, 16 i + 16) after `lds` (wave-uniform).  Kept out of templates:
+// the host compilation pass drops a template kernel's launch stub when the
+// builtin appears in its body.
+__device__ __forceinline__ void lds_dma16(const float* src, KDA_LDS void* lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// N consecutive elements of one LDS row, stored with as few instructions as
+// the alignment (N elements of type T are N * sizeof(T)-byte aligned) allows.
+template <int N>
+__device__ __forceinline__ void lds_store_run(KDA_LDS __bf16* p, const float (&v)[N]) {
+    if constexpr (N == 1) {
+        *p = (__bf16)v[0];
+    } else {
+        typedef __attribute__((ext_vector_type(N))) __bf16 vec_t;
+        vec_t x;
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = (__bf16)v[i];
+        *reinterpret_cast<KDA_LDS vec_t*>(p) = x;
+    }
+}
+template <int N>
+__device__ __forceinline__ void lds_store_run(KDA_LDS float* p, const float (&v)[N]) {
+    if constexpr (N == 1) {
+        *p = v[0];
+    } else if constexpr (N <= 4) {
+        typedef __attribute__((ext_vector_type(N))) float vec_t;
+        vec_t x;
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = v[i];
+        *reinterpret_cast<KDA_LDS vec_t*>(p) = x;
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 4)
+            *reinterpret_cast<KDA_LDS f32x4_t*>(p + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
+    }
+}
+
+// A lane-dependent value pinned in a register: the compiler may not recompute
+// it where it is used (inside the chunk loop that would reintroduce runtime
+// multiplies into LDS addressing).
+__device__ __forceinline__ int pinned(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
 // Two stacked accumulator tiles (rows 0..15 and 16..31 of a 32-block) as a B
@@ -108,32 +182,18 @@ __device__ __forceinline__ void acc_pair_frag(Frag<OpT>& f, const f32x4_t& lo, c
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}; }
 
-// Two adjacent input elements (a channel pair) as fp32.
-template <typename T> struct Pair;
-template <> struct Pair<__bf16> {
-    typedef uint32_t raw;
-    __device__ __forceinline__ static raw load(const __bf16* p) { return *reinterpret_cast<const uint32_t*>(p); }
-    __device__ __forceinline__ static float lo(raw r) { return __uint_as_float(r << 16); }
-    __device__ __forceinline__ static float hi(raw r) { return __uint_as_float(r & 0xffff0000u); }
-    __device__ __forceinline__ static raw zero() { return 0u; }
-};
-template <> struct Pair<float> {
-    typedef float2 raw;
-    __device__ __forceinline__ static raw load(const float* p) { return *reinterpret_cast<const float2*>(p); }
-    __device__ __forceinline__ static float lo(raw r) { return r.x; }
-    __device__ __forceinline__ static float hi(raw r) { return r.y; }
-    __device__ __forceinline__ static raw zero() { return make_float2(0.0f, 0.0f); }
-};
-
-// Store two values as an adjacent pair of OpT in LDS.
-__device__ __forceinline__ void st_pair(__bf16* p, float a, float b) {
-    bf16x2_t v;
-    v[0] = (__bf16)a;
-    v[1] = (__bf16)b;
-    *reinterpret_cast<bf16x2_t*>(p) = v;
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
+// not for its global loads in flight (a __syncthreads() fence would drain those
+// too and expose a prefetch's full latency).  The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-__device__ __forceinline__ void st_pair(float* p, float a, float b) {
-    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+
+// Workgroup barrier that also waits for this wave's global loads, including
+// loads that write LDS directly.
+__device__ __forceinline__ void barrier_all() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 }  // namespace kda

@@ -47,23 +47,31 @@ struct PrefillCfg {
     static constexpr int NT = C / 16;            // 16-token row tiles per chunk
     static constexpr int NTB = (NT + 1) / 2;     // 32-token contraction blocks per chunk
     static constexpr int DVW = 64 * NCT;         // state columns per workgroup
-    static constexpr int NPAIR = DK / 2;         // channel pairs (decay phase)
-    static constexpr int NSEG = 256 / NPAIR;     // token segments (decay phase)
+    static constexpr int NQ = DK / 4;            // channel quads (decay phase)
+    static constexpr int NSEG = 256 / NQ;        // token segments (decay phase)
     static constexpr int TPS = C / NSEG;         // tokens per segment
     static constexpr int SPT = 16 / TPS;         // segments per 16-token tile
     static constexpr int CP = C < 32 ? 32 : C;   // token extent of token-indexed rows
     static constexpr int PADE = sizeof(OpT) == 2 ? 8 : 4;
     static constexpr int PK = DK + PADE;         // pitch of [C][DK] operand arrays
-    static constexpr int PT = CP + PADE;         // pitch of sT, sB, sKpT
-    static constexpr int PV = DVW + PADE;        // pitch of sV / sO
-    static constexpr int PA = C + 1;             // pitch of fp32 sA / sTf
+    static constexpr int PT = CP + PADE;         // pitch of sTA, sB, sKpT
+    static constexpr int PV = DVW + PADE;        // pitch of sV
+    static constexpr int PW = 16 * NCT + PADE;   // pitch of a wave's output staging
+    static constexpr int PD = 20;                // pitch of the transposed fp32 diagonal A blocks
+    static constexpr int PDB = 16 * PD + 16;     // stride between diagonal blocks (bank offset 16)
     static constexpr int VEL = 16 / (int)sizeof(TIn);           // elements per 16-byte vector
     static constexpr int VPR = DVW / VEL;                       // vectors per value row
     static constexpr int NV = C * VPR;                          // vectors per value chunk
     static constexpr int NVV = (NV + 255) / 256;                // vectors per thread
+    static constexpr int VPRW = 16 * NCT / VEL;                 // vectors per wave output row
+    static constexpr int NOT = 16 * VPRW;                       // vectors per wave output tile
+    static constexpr int NOTL = (NOT + 63) / 64;                // per lane
+    static constexpr int NDMA = C * DK * 4 / 1024;              // 1 KiB log-decay loads per chunk
+    static constexpr int NQT = C * DK / 4;                      // quads per [C][DK] array
 
     static_assert(TPS >= 1 && 16 % TPS == 0, "segment must sit inside one tile");
-    static_assert(DK % 32 == 0 && C % 16 == 0, "shape");
+    static_assert(DK % 32 == 0 && C % 16 == 0 && NT <= 4, "shape");
+    static_assert(NDMA % 4 == 0, "log-decay loads split evenly over the 4 waves");
 
     static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t oLq = 0;
@@ -71,47 +79,85 @@ struct PrefillCfg {
     static constexpr size_t oKd = oLk + al(sizeof(OpT) * C * PK);
     static constexpr size_t oKpT = oKd + al(sizeof(OpT) * C * PK);
     static constexpr size_t oV = oKpT + al(sizeof(OpT) * DK * PT);
-    static constexpr size_t oT = oV + al(sizeof(TIn) * C * PV);
-    static constexpr size_t oB = oT + al(sizeof(OpT) * C * PT);
-    static constexpr size_t oA = oB + al(sizeof(OpT) * C * PT);
-    static constexpr size_t oTf = oA + al(4 * C * PA);
-    static constexpr size_t oM = oTf + al(4 * C * PA);
-    static constexpr size_t oE = oM + al(4 * 3 * 16 * 17);
+    static constexpr size_t oTA = oV + al(sizeof(TIn) * C * PV);
+    static constexpr size_t oB = oTA + al(sizeof(OpT) * C * PT);
+    static constexpr size_t oAd = oB + al(sizeof(OpT) * C * PT);
+    static constexpr size_t oE = oAd + al(4 * NT * PDB);
     static constexpr size_t oD = oE + al(4 * (NT + 1) * DK);
     static constexpr size_t oBeta = oD + al(4 * NT * DK);
     static constexpr size_t oTot = oBeta + al(4 * C);
-    static constexpr size_t LDS = oTot + al(4 * NSEG * DK);
-    static_assert(sizeof(TIn) * PV <= sizeof(OpT) * PK, "output staging aliases sLk");
+    static constexpr size_t oO = oTot + al(4 * NSEG * DK);
+    static constexpr size_t LDS = oO + al(sizeof(TIn) * 4 * 16 * PW);
+    static_assert(LDS + 4 * C * DK <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+};
+
+// Row tile of the pi-th (row, column <= row) tile pair, pairs enumerated row by row.
+constexpr int pair_row(int pi) {
+    int ar = 0;
+    while ((ar + 1) * (ar + 2) / 2 <= pi) ++ar;
+    return ar;
+}
+
+// Four adjacent elements (a channel quad) of an input or operand array.
+template <typename T> struct Quad;
+template <> struct Quad<__bf16> {
+    typedef u32x2_t raw;
+    __device__ __forceinline__ static raw load(const __bf16* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+    __device__ __forceinline__ static raw load(const KDA_LDS __bf16* p) { return *reinterpret_cast<const KDA_LDS u32x2_t*>(p); }
+    __device__ __forceinline__ static float get(raw r, int i) {
+        const uint32_t w = i < 2 ? r[0] : r[1];
+        return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    __device__ __forceinline__ static void store(KDA_LDS __bf16* p, float a, float b, float c, float d) {
+        bf16x4_t v;
+        v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+        *reinterpret_cast<KDA_LDS bf16x4_t*>(p) = v;
+    }
+};
+template <> struct Quad<float> {
+    typedef f32x4_t raw;
+    __device__ __forceinline__ static raw load(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
+    __device__ __forceinline__ static raw load(const KDA_LDS float* p) { return *reinterpret_cast<const KDA_LDS f32x4_t*>(p); }
+    __device__ __forceinline__ static float get(raw r, int i) { return r[i]; }
+    __device__ __forceinline__ static void store(KDA_LDS float* p, float a, float b, float c, float d) {
+        *reinterpret_cast<KDA_LDS f32x4_t*>(p) = f32x4_t{a, b, c, d};
+    }
 };
 
 template <class Cfg>
 __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a) {
     using TIn = typename Cfg::TIn;
     using OpT = typename Cfg::OpT;
-    using P2 = Pair<TIn>;
+    using QI = Quad<TIn>;
+    using QO = Quad<OpT>;
     constexpr int DK = Cfg::DK, C = Cfg::C, NT = Cfg::NT, NTB = Cfg::NTB, NCT = Cfg::NCT;
-    constexpr int DVW = Cfg::DVW, NPAIR = Cfg::NPAIR, NSEG = Cfg::NSEG, TPS = Cfg::TPS;
-    constexpr int SPT = Cfg::SPT, CP = Cfg::CP, PK = Cfg::PK, PT = Cfg::PT, PV = Cfg::PV;
-    constexpr int PA = Cfg::PA, VEL = Cfg::VEL, VPR = Cfg::VPR, NV = Cfg::NV, NVV = Cfg::NVV;
+    constexpr int DVW = Cfg::DVW, NQ = Cfg::NQ, NSEG = Cfg::NSEG, TPS = Cfg::TPS;
+    constexpr int SPT = Cfg::SPT, PK = Cfg::PK, PT = Cfg::PT, PV = Cfg::PV, PW = Cfg::PW;
+    constexpr int PD = Cfg::PD, PDB = Cfg::PDB, VEL = Cfg::VEL, VPR = Cfg::VPR, NV = Cfg::NV, NVV = Cfg::NVV;
+    constexpr int VPRW = Cfg::VPRW, NOT = Cfg::NOT, NOTL = Cfg::NOTL, NDMA = Cfg::NDMA;
+    constexpr int NQT = Cfg::NQT;
     constexpr int NIT = DK / 16;   // 16-row tiles of the state
     constexpr int NKB = DK / 32;   // 32-channel contraction blocks
 
-    __shared__ __align__(16) char smem[Cfg::LDS];
-    OpT* sLq = reinterpret_cast<OpT*>(smem + Cfg::oLq);
-    OpT* sLk = reinterpret_cast<OpT*>(smem + Cfg::oLk);
-    OpT* sKd = reinterpret_cast<OpT*>(smem + Cfg::oKd);
-    OpT* sKpT = reinterpret_cast<OpT*>(smem + Cfg::oKpT);
-    TIn* sV = reinterpret_cast<TIn*>(smem + Cfg::oV);
-    OpT* sT = reinterpret_cast<OpT*>(smem + Cfg::oT);
-    OpT* sB = reinterpret_cast<OpT*>(smem + Cfg::oB);
-    float* sA = reinterpret_cast<float*>(smem + Cfg::oA);
-    float* sTf = reinterpret_cast<float*>(smem + Cfg::oTf);
-    float* sM = reinterpret_cast<float*>(smem + Cfg::oM);
-    float* sE = reinterpret_cast<float*>(smem + Cfg::oE);
-    float* sD = reinterpret_cast<float*>(smem + Cfg::oD);
-    float* sBeta = reinterpret_cast<float*>(smem + Cfg::oBeta);
-    float* sTot = reinterpret_cast<float*>(smem + Cfg::oTot);
-    TIn* sO = reinterpret_cast<TIn*>(smem + Cfg::oLk);  // aliases sLk after the X/P products
+    __shared__ __align__(16) char smem_[Cfg::LDS];
+    KDA_LDS char* smem = (KDA_LDS char*)smem_;
+    KDA_LDS OpT* sLq = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oLq);     // q 2^{g - rho}, then Q~ = q 2^{g}
+    KDA_LDS OpT* sLk = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oLk);     // k 2^{g - rho}, then K~ = k 2^{g}
+    KDA_LDS OpT* sKd = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oKd);     // k 2^{rho - g}
+    KDA_LDS OpT* sKpT = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oKpT);   // (k 2^{g_C - g})^T
+    KDA_LDS TIn* sV = reinterpret_cast<KDA_LDS TIn*>(smem + Cfg::oV);
+    KDA_LDS OpT* sTA = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oTA);     // diagonal blocks T_aa, below them -beta A
+    KDA_LDS OpT* sB = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oB);       // decay-weighted Q K^T, inclusive lower
+    KDA_LDS float* sAd = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oAd); // beta A of the diagonal blocks, transposed
+    KDA_LDS float* sE = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oE);
+    KDA_LDS float* sD = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oD);
+    KDA_LDS float* sBeta = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oBeta);
+    KDA_LDS float* sTot = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oTot);
+    KDA_LDS TIn* sO = reinterpret_cast<KDA_LDS TIn*>(smem + Cfg::oO);
+    // raw log-decay of the next chunk, written by direct global->LDS loads; a separate object so
+    // that the compiler can tell those writes never alias the arrays above
+    __shared__ __align__(16) float sLam_[C * DK];
+    KDA_LDS float* sLam = (KDA_LDS float*)sLam_;
 
     // ---- unit of this workgroup; sibling column slices share an XCD (blockIdx % 8) ----
     const int bid = blockIdx.x;
@@ -145,187 +191,260 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
 
     // ---- initial state: lane holds S[16*it + 4*lg + j][colw(ct)] ----
     f32x4_t st[NIT][NCT];
-    {
-        const float* sin = (a.init_mode == 1)
-            ? a.s_in + (long long)bh * a.sin_bh_stride + (long long)s * a.sin_seg_stride
-            : nullptr;
+    if (a.init_mode == 1) {
+        const float* sin = a.s_in + (long long)bh * a.sin_bh_stride + (long long)s * a.sin_seg_stride;
 #pragma unroll
         for (int it = 0; it < NIT; ++it)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 const int col = col0 + wave * 16 * NCT + ct * 16 + lr;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = 16 * it + 4 * lg + j;
-                    float x = 0.0f;
-                    if (a.init_mode == 1) x = sin[(long long)row * DK + col];
-                    else if (a.init_mode == 2) x = (row == col) ? 1.0f : 0.0f;
-                    st[it][ct][j] = x;
-                }
+                for (int j = 0; j < 4; ++j) st[it][ct][j] = sin[(long long)(16 * it + 4 * lg + j) * DK + col];
+            }
+    } else {
+        const bool ident = a.init_mode == 2;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int col = col0 + wave * 16 * NCT + ct * 16 + lr;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st[it][ct][j] = (ident && 16 * it + 4 * lg + j == col) ? 1.0f : 0.0f;
             }
     }
 
-    // ---- zero the token-padded operand arrays once (never-written parts stay zero) ----
+    // ---- zero the token-padded operand arrays once (parts never written stay zero) ----
     for (int e = tid; e < C * PT; e += 256) {
-        sT[e] = from_f32<OpT>(0.0f);
+        sTA[e] = from_f32<OpT>(0.0f);
         sB[e] = from_f32<OpT>(0.0f);
     }
     for (int e = tid; e < DK * PT; e += 256) sKpT[e] = from_f32<OpT>(0.0f);
 
-    // ---- decay-phase thread mapping: channel pair cp, token segment sg ----
-    const int cp = tid % NPAIR;
-    const int sg = tid / NPAIR;
-    const int ch0 = 2 * cp;
+    // ---- decay-phase thread mapping: channel quad cq, token segment sg ----
+    const int cq = tid % NQ;
+    const int sg = tid / NQ;
+    const int ch0 = 4 * cq;
 
-    // ---- prefetch registers for the next chunk ----
-    typename P2::raw pq[TPS], pk[TPS];
-    float2 pl[TPS];
+    // ---- lane-dependent LDS offsets (elements), computed once: the chunk loop adds only constants ----
+    const int oA = pinned(sg * TPS * PK + ch0);                   // this thread's rows of [C][PK] arrays
+    const int oKp = pinned(ch0 * PT + sg * TPS);                  // this thread's K'^T entries
+    const int oLam = pinned(sg * TPS * DK + ch0);                 // this thread's raw log-decay
+    const int oVc = pinned((tid / VPR) * PV + (tid % VPR) * VEL); // value commit
+    const int oK = pinned(lr * PK + 4 * lg);                      // fragment row, [*][PK] arrays
+    const int oT = pinned(lr * PT + 4 * lg);                      // fragment row, [*][PT] arrays
+    const int oW = pinned(4 * lg * PT + lr);                      // accumulator element, [*][PT] arrays
+    const int oAd = pinned(lr * PD + 4 * lg);                     // transposed diagonal-block store
+    const int oAdT = pinned((lane >> 4) * PDB);                   // diagonal block of this lane (wave 0)
+    const int oE1 = pinned((lane >> 4) * 16 * (PT + 1) + (lane & 15));  // T_aa column of this lane (wave 0)
+    const int oV = pinned(4 * lg * PV + wave * 16 * NCT + lr);    // value in accumulator layout
+    const int oOw = pinned(wave * 16 * PW + 4 * lg * PW + lr);    // output staging write
+    const int oOr = pinned(wave * 16 * PW + (lane / VPRW) * PW + (lane % VPRW) * VEL);  // staging read
+    const int tq = tid - 64;                                      // waves 1..3: in-place operand scaling
+    const int oCv = pinned((tq / (DK / 4)) * PK + 4 * (tq % (DK / 4)));
+    const int cvRow0 = tq / (DK / 4);
+    const int cvC4 = 4 * (tq % (DK / 4));
+    constexpr int CV_ROWS = 192 / (DK / 4);                       // rows advanced per step
+    const long long oGo = (long long)(lane / VPRW) * HD + wave * 16 * NCT + (lane % VPRW) * VEL;
+
+    // ---- per-lane global bases: inside the loop only a uniform (c0 + const) * stride is added ----
+    const TIn* gq_l = gq + (long long)(sg * TPS) * HD + ch0;
+    const TIn* gk_l = gk + (long long)(sg * TPS) * HD + ch0;
+    const float* gb_l = gbeta + (long long)(tid % C) * a.H;
+    const int v_row = tid / VPR, v_off = (tid % VPR) * VEL;
+    const TIn* gv_l = gv + (long long)v_row * HD + v_off;
+    const int d_row = (4 * lane) / DK, d_col = (4 * lane) % DK;   // this lane's 16 bytes of a 1 KiB block
+    const float* gla_l = gla + (long long)d_row * HD + d_col;
+    constexpr int D_ROWS = 256 / DK;                               // rows per 1 KiB block
+
+    // ---- prefetch of the next chunk: log-decay straight into LDS, the rest into registers ----
+    typename QI::raw pq[TPS], pk[TPS];
     float pbeta = 0.0f;
-    uint4 pv[NVV];
+    u32x4_t pv[NVV];
+    auto clampt = [&](long long t) { return t < t_end ? t : t_end - 1; };
 
-    auto load_chunk = [&](long long c0) {
+    // Loads only: in a partial last chunk, rows past the end of the unit read the last valid row
+    // (in bounds) and are zeroed when the chunk is consumed, so no select waits on a load in
+    // flight.  A zero key, value, query, beta and log-decay is an exact identity on the state.
+    auto load_decay = [&](long long c0) {
+        if (c0 + C <= t_end) {
 #pragma unroll
-        for (int i = 0; i < TPS; ++i) {
-            const long long t = c0 + sg * TPS + i;
-            if (t < t_end) {
-                const long long off = t * HD + ch0;
-                pl[i] = *reinterpret_cast<const float2*>(gla + off);
-                pq[i] = P2::load(gq + off);
-                pk[i] = P2::load(gk + off);
-            } else {
-                pl[i] = make_float2(0.0f, 0.0f);
-                pq[i] = P2::zero();
-                pk[i] = P2::zero();
+            for (int m = 0; m < NDMA / 4; ++m) {
+                const int gi = wave * (NDMA / 4) + m;
+                lds_dma16(gla_l + (c0 + gi * D_ROWS) * HD, (KDA_LDS void*)(sLam + gi * 256));
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < NDMA / 4; ++m) {
+                const int gi = wave * (NDMA / 4) + m;
+                lds_dma16(gla + clampt(c0 + gi * D_ROWS + d_row) * HD + d_col, (KDA_LDS void*)(sLam + gi * 256));
             }
         }
-        if (tid < C) {
-            const long long t = c0 + tid;
-            pbeta = (t < t_end) ? gbeta[t * a.H] : 0.0f;
-        }
+    };
+    auto load_rest = [&](long long c0) {
+        if (c0 + C <= t_end) {
 #pragma unroll
-        for (int m = 0; m < NVV; ++m) {
-            const int e = tid + 256 * m;
-            uint4 x = make_uint4(0u, 0u, 0u, 0u);
-            if (e < NV) {
-                const int row = e / VPR, cv = e % VPR;
-                const long long t = c0 + row;
-                if (t < t_end && !zero_v)
-                    x = *reinterpret_cast<const uint4*>(gv + t * HD + cv * VEL);
+            for (int i = 0; i < TPS; ++i) {
+                pq[i] = QI::load(gq_l + (c0 + i) * HD);
+                pk[i] = QI::load(gk_l + (c0 + i) * HD);
             }
-            pv[m] = x;
+            pbeta = gb_l[c0 * a.H];
+            if (!zero_v) {
+#pragma unroll
+                for (int m = 0; m < NVV; ++m)
+                    if (NV % 256 == 0 || tid + 256 * m < NV)
+                        pv[m] = *reinterpret_cast<const u32x4_t*>(gv_l + (c0 + m * (256 / VPR)) * HD);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TPS; ++i) {
+                const long long off = clampt(c0 + sg * TPS + i) * HD + ch0;
+                pq[i] = QI::load(gq + off);
+                pk[i] = QI::load(gk + off);
+            }
+            pbeta = gbeta[clampt(c0 + (tid % C)) * a.H];
+            if (!zero_v) {
+#pragma unroll
+                for (int m = 0; m < NVV; ++m)
+                    if (NV % 256 == 0 || tid + 256 * m < NV)
+                        pv[m] = *reinterpret_cast<const u32x4_t*>(gv + clampt(c0 + v_row + m * (256 / VPR)) * HD + v_off);
+            }
         }
     };
 
     const long long ntok = t_end - t_begin;
     const int nchunks = ntok > 0 ? (int)((ntok + C - 1) / C) : 0;
-    if (nchunks > 0) load_chunk(t_begin);
+    if (nchunks > 0) {
+        load_decay(t_begin);
+        load_rest(t_begin);
+    }
 
     for (int c = 0; c < nchunks; ++c) {
         const long long c0 = t_begin + (long long)c * C;
-        __syncthreads();  // every read of the previous chunk's LDS is done
+        barrier_all();  // every wave's log-decay block has landed; the previous chunk's LDS reads are done
 
-        // ================= A: commit prefetch, per-segment cumulative decay =================
+        // ================= A: commit prefetched values, per-segment cumulative decay =================
 #pragma unroll
         for (int m = 0; m < NVV; ++m) {
             const int e = tid + 256 * m;
-            if (e < NV) {
-                const int row = e / VPR, cv = e % VPR;
-                *reinterpret_cast<uint4*>(sV + row * PV + cv * VEL) = pv[m];
+            if (NV % 256 == 0 || e < NV) {
+                const bool ok = !zero_v && c0 + e / VPR < t_end;
+                const u32x4_t x = pv[m];
+                *reinterpret_cast<KDA_LDS u32x4_t*>(sV + oVc + m * (256 / VPR) * PV) =
+                    u32x4_t{ok ? x[0] : 0u, ok ? x[1] : 0u, ok ? x[2] : 0u, ok ? x[3] : 0u};
             }
         }
-        if (tid < C) sBeta[tid] = pbeta;
+        if (tid < C) sBeta[tid] = (c0 + tid < t_end) ? pbeta : 0.0f;
 
-        float g0[TPS], g1[TPS], kx0[TPS], kx1[TPS], qx0[TPS], qx1[TPS];
+        bool okt[TPS];
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) okt[i] = c0 + sg * TPS + i < t_end;
+        float g[TPS][4];
         {
-            float run0 = 0.0f, run1 = 0.0f;
+            float run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
-                const float l0 = fminf(fmaxf(pl[i].x, kLogAlphaMin), 0.0f) * kLog2e;
-                const float l1 = fminf(fmaxf(pl[i].y, kLogAlphaMin), 0.0f) * kLog2e;
-                run0 += l0;
-                run1 += l1;
-                g0[i] = run0;
-                g1[i] = run1;
-                qx0[i] = P2::lo(pq[i]);
-                qx1[i] = P2::hi(pq[i]);
-                kx0[i] = P2::lo(pk[i]);
-                kx1[i] = P2::hi(pk[i]);
+                const f32x4_t l4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sLam + oLam + i * DK);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    run[u] += okt[i] ? fminf(fmaxf(l4[u], kLogAlphaMin), 0.0f) * kLog2e : 0.0f;
+                    g[i][u] = run[u];
+                }
             }
-            sTot[sg * DK + ch0] = run0;
-            sTot[sg * DK + ch0 + 1] = run1;
+            *reinterpret_cast<KDA_LDS f32x4_t*>(sTot + sg * DK + ch0) = f32x4_t{run[0], run[1], run[2], run[3]};
         }
-        __syncthreads();
-        if (c + 1 < nchunks) load_chunk(c0 + C);  // overlaps with everything below
+        barrier_lds();
+        // the raw log-decay of this chunk is consumed: fetch the next chunk's behind everything below
+        if (c + 1 < nchunks) load_decay(c0 + C);
 
         // ================= A': references and decay-scaled operands =================
         {
             // prefix over segments, summed in the same order by every thread
-            float P0[NSEG + 1], P1[NSEG + 1];
-            P0[0] = 0.0f;
-            P1[0] = 0.0f;
+            f32x4_t P[NSEG + 1];
+            P[0] = zero4();
 #pragma unroll
-            for (int q2 = 0; q2 < NSEG; ++q2) {
-                P0[q2 + 1] = P0[q2] + sTot[q2 * DK + ch0];
-                P1[q2 + 1] = P1[q2] + sTot[q2 * DK + ch0 + 1];
-            }
+            for (int q2 = 0; q2 < NSEG; ++q2)
+                P[q2 + 1] = P[q2] + *reinterpret_cast<const KDA_LDS f32x4_t*>(sTot + q2 * DK + ch0);
             const int at = (sg * TPS) / 16;       // this segment's row tile
-            float off0 = 0.0f, off1 = 0.0f, rho0 = 0.0f, rho1 = 0.0f, nx0 = 0.0f, nx1 = 0.0f;
+            f32x4_t off = zero4(), rho = zero4(), nx = zero4();
 #pragma unroll
             for (int q2 = 0; q2 <= NSEG; ++q2) {
-                if (q2 == sg) { off0 = P0[q2]; off1 = P1[q2]; }
-                if (q2 == at * SPT) { rho0 = P0[q2]; rho1 = P1[q2]; }
-                if (q2 == (at + 1) * SPT) { nx0 = P0[q2]; nx1 = P1[q2]; }
+                if (q2 == sg) off = P[q2];
+                if (q2 == at * SPT) rho = P[q2];
+                if (q2 == (at + 1) * SPT) nx = P[q2];
             }
-            const float gC0 = P0[NSEG], gC1 = P1[NSEG];
-            const float fd0 = fast_exp2(nx0 - rho0), fd1 = fast_exp2(nx1 - rho1);  // [2^-115.4, 1]
-            const float fc0 = fast_exp2(gC0 - nx0), fc1 = fast_exp2(gC1 - nx1);    // (0, 1]
+            const f32x4_t gC = P[NSEG];
+            float fd[4], fc[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                fd[u] = fast_exp2(nx[u] - rho[u]);   // 2^{rho_{a+1} - rho_a} in [2^-115.4, 1]
+                fc[u] = fast_exp2(gC[u] - nx[u]);    // 2^{g_C - rho_{a+1}} in (0, 1]
+            }
+            float kp[4][TPS];   // K' of this thread's channels, by channel: one vector store each
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
-                const int r = sg * TPS + i;
-                const float gg0 = g0[i] + off0, gg1 = g1[i] + off1;
-                const float x0 = fast_exp2(gg0 - rho0), x1 = fast_exp2(gg1 - rho1);  // <= 1
-                const float y0 = fast_exp2(rho0 - gg0), y1 = fast_exp2(rho1 - gg1);  // >= 1
-                st_pair(sLq + r * PK + ch0, qx0[i] * x0, qx1[i] * x1);
-                st_pair(sLk + r * PK + ch0, kx0[i] * x0, kx1[i] * x1);
-                st_pair(sKd + r * PK + ch0, kx0[i] * y0, kx1[i] * y1);
-                sKpT[ch0 * PT + r] = from_f32<OpT>(kx0[i] * ((y0 * fd0) * fc0));
-                sKpT[(ch0 + 1) * PT + r] = from_f32<OpT>(kx1[i] * ((y1 * fd1) * fc1));
+                float lq[4], lk[4], kd[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float gg = g[i][u] + off[u];
+                    const float x = fast_exp2(gg - rho[u]);  // <= 1
+                    const float y = fast_exp2(rho[u] - gg);  // >= 1, at most 2^115.4 = e^80
+                    const float qv = okt[i] ? QI::get(pq[i], u) : 0.0f;
+                    const float kv = okt[i] ? QI::get(pk[i], u) : 0.0f;
+                    lq[u] = qv * x;
+                    lk[u] = kv * x;
+                    kd[u] = kv * y;
+                    // K' = k 2^{g_C - g}: the factor above 1 meets only a factor that cannot underflow
+                    kp[u][i] = kv * ((y * fd[u]) * fc[u]);
+                }
+                QO::store(sLq + oA + i * PK, lq[0], lq[1], lq[2], lq[3]);
+                QO::store(sLk + oA + i * PK, lk[0], lk[1], lk[2], lk[3]);
+                QO::store(sKd + oA + i * PK, kd[0], kd[1], kd[2], kd[3]);
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) lds_store_run<TPS>(sKpT + oKp + u * PT, kp[u]);
             if (sg == 0) {
 #pragma unroll
                 for (int t2 = 0; t2 <= NT; ++t2) {
-                    sE[t2 * DK + ch0] = fast_exp2(P0[t2 * SPT]);
-                    sE[t2 * DK + ch0 + 1] = fast_exp2(P1[t2 * SPT]);
-                    if (t2 < NT) {
-                        sD[t2 * DK + ch0] = fast_exp2(P0[(t2 + 1) * SPT] - P0[t2 * SPT]);
-                        sD[t2 * DK + ch0 + 1] = fast_exp2(P1[(t2 + 1) * SPT] - P1[t2 * SPT]);
+                    f32x4_t e4, d4;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        e4[u] = fast_exp2(P[t2 * SPT][u]);
+                        d4[u] = t2 < NT ? fast_exp2(P[(t2 + 1) * SPT][u] - P[t2 * SPT][u]) : 0.0f;
                     }
+                    *reinterpret_cast<KDA_LDS f32x4_t*>(sE + t2 * DK + ch0) = e4;
+                    if (t2 < NT) *reinterpret_cast<KDA_LDS f32x4_t*>(sD + t2 * DK + ch0) = d4;
                 }
             }
         }
-        __syncthreads();
+        // the raw q, k, v of this chunk are consumed: fetch the next chunk's
+        if (c + 1 < nchunks) load_rest(c0 + C);
+        barrier_lds();
 
         // ================= B: decay-weighted KK^T and QK^T tiles =================
         {
             constexpr int NP = NT * (NT + 1) / 2;
-            for (int pi = wave; pi < NP; pi += 4) {
-                int ar = 0, rem = pi;
-                while (rem > ar) { rem -= ar + 1; ++ar; }
-                const int ac = rem;
+            static_for<0, NP>([&](auto PIc) {
+                constexpr int pi = decltype(PIc)::value;
+                constexpr int ar = pair_row(pi);
+                constexpr int ac = pi - ar * (ar + 1) / 2;
+                if (pi % 4 != wave) return;   // wave-uniform
                 f32x4_t accA = zero4(), accB = zero4();
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     Frag<OpT> fk, fq, fr;
-                    lds_row_frag(fk, sLk + (16 * ar + lr) * PK + 32 * kb, lg);
-                    lds_row_frag(fq, sLq + (16 * ar + lr) * PK + 32 * kb, lg);
-                    lds_row_frag(fr, sKd + (16 * ac + lr) * PK + 32 * kb, lg);
-                    if (ac < ar) {
+                    frag_ld(fk, sLk + 16 * ar * PK + 32 * kb + oK);
+                    frag_ld(fq, sLq + 16 * ar * PK + 32 * kb + oK);
+                    frag_ld(fr, sKd + 16 * ac * PK + 32 * kb + oK);
+                    if constexpr (ac < ar) {
+                        // R = Kd 2^{rho_ar - rho_ac}: multiply by 2^{rho_{m+1} - rho_m} one tile at a
+                        // time, the first step bringing Kd (up to 2^115) down to at most 1
                         float val[8];
 #pragma unroll
                         for (int j = 0; j < 8; ++j) val[j] = fr.get(j);
+#pragma unroll
                         for (int m = ac; m < ar; ++m) {
                             float d8[8];
-                            lds_row_f32x8(d8, sD + m * DK + 32 * kb, lg);
+                            f32x8_ld(d8, sD + m * DK + 32 * kb + 4 * lg);
 #pragma unroll
                             for (int j = 0; j < 8; ++j) val[j] *= d8[j];
                         }
@@ -335,171 +454,186 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
                     accA = mma(fk, fr, accA);
                     accB = mma(fq, fr, accB);
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * ar + 4 * lg + j;
-                    const int i = 16 * ac + lr;
-                    float av = accA[j] * sBeta[r];
-                    float bv = accB[j];
-                    if (ac == ar) {
-                        av = (i < r) ? av : 0.0f;
-                        bv = (i <= r) ? bv : 0.0f;
-                    }
-                    sA[r * PA + i] = av;
-                    sB[r * PT + i] = from_f32<OpT>(bv);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ================= C: T = (I + A)^{-1} =================
-        if (wave == 0) {
-            const int ab = lane >> 4, jj = lane & 15;
-            if (ab < NT) {
-                const float* Ab = sA + (16 * ab) * PA + 16 * ab;
-                float col[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float acc = (r == jj) ? 1.0f : 0.0f;
-#pragma unroll
-                    for (int i = 0; i < r; ++i) acc -= Ab[r * PA + i] * col[i];
-                    col[r] = acc;
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sTf[(16 * ab + r) * PA + 16 * ab + jj] = col[r];
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int d = 1; d < NT; ++d) {
-            const int nb = NT - d;
-            for (int e = tid; e < nb * 256; e += 256) {
-                const int bi = e >> 8, r = (e >> 4) & 15, jj = e & 15;
-                const int ar = d + bi, bc = bi;
-                float acc = 0.0f;
-                for (int cc = bc; cc < ar; ++cc) {
-                    const float* Ar = sA + (16 * ar + r) * PA + 16 * cc;
-                    const float* Tc = sTf + (16 * cc) * PA + 16 * bc + jj;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc += Ar[i] * Tc[i * PA];
-                }
-                sM[(bi * 16 + r) * 17 + jj] = acc;
-            }
-            __syncthreads();
-            for (int e = tid; e < nb * 256; e += 256) {
-                const int bi = e >> 8, r = (e >> 4) & 15, jj = e & 15;
-                const int ar = d + bi, bc = bi;
-                const float* Tr = sTf + (16 * ar + r) * PA + 16 * ar;
-                float acc = 0.0f;
-#pragma unroll
-                for (int m = 0; m < 16; ++m) acc += Tr[m] * sM[(bi * 16 + m) * 17 + jj];
-                sTf[(16 * ar + r) * PA + 16 * bc + jj] = -acc;
-            }
-            __syncthreads();
-        }
-        for (int e = tid; e < C * C; e += 256) {
-            const int r = e / C, cc = e % C;
-            sT[r * PT + cc] = from_f32<OpT>(cc <= r ? sTf[r * PA + cc] : 0.0f);
-        }
-        __syncthreads();
-
-        // ================= D: state-dependent products =================
-        f32x4_t X[NT][NCT], Pq[NT][NCT];
-        {
-            Frag<OpT> fs[NKB][NCT];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) acc_pair_frag(fs[kb][ct], st[2 * kb][ct], st[2 * kb + 1][ct], true);
-#pragma unroll
-            for (int ar = 0; ar < NT; ++ar) {
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) { X[ar][ct] = zero4(); Pq[ar][ct] = zero4(); }
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    Frag<OpT> fk, fq;
-                    float e8[8];
-                    lds_row_frag(fk, sLk + (16 * ar + lr) * PK + 32 * kb, lg);
-                    lds_row_frag(fq, sLq + (16 * ar + lr) * PK + 32 * kb, lg);
-                    lds_row_f32x8(e8, sE + ar * DK + 32 * kb, lg);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        fk.set(j, fk.get(j) * e8[j]);
-                        fq.set(j, fq.get(j) * e8[j]);
-                    }
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        X[ar][ct] = mma(fk, fs[kb][ct], X[ar][ct]);
-                        Pq[ar][ct] = mma(fq, fs[kb][ct], Pq[ar][ct]);
-                    }
-                }
-            }
-        }
-        __syncthreads();  // sLk / sLq reads done: sO may now overwrite sLk
-
-        // RHS = beta (V - X), then U = T RHS
-        Frag<OpT> fU[NTB][NCT];
-        {
-            f32x4_t Rh[NT][NCT];
-#pragma unroll
-            for (int ar = 0; ar < NT; ++ar)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const int wc = wave * 16 * NCT + ct * 16 + lr;
+                const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sBeta + 16 * ar + 4 * lg);
+                if constexpr (ac == ar) {
+                    f32x4_t ad;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int r = 16 * ar + 4 * lg + j;
-                        const float vv = zero_v ? 0.0f : to_f32<TIn>(sV[r * PV + wc]);
-                        Rh[ar][ct][j] = sBeta[r] * (vv - X[ar][ct][j]);
+                        const int rl = 4 * lg + j;
+                        ad[j] = (lr < rl) ? accA[j] * bt4[j] : 0.0f;
+                        sB[16 * ar * PT + 16 * ac + j * PT + oW] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
+                    }
+                    *reinterpret_cast<KDA_LDS f32x4_t*>(sAd + ar * PDB + oAd) = ad;  // transposed
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        sTA[16 * ar * PT + 16 * ac + j * PT + oW] = from_f32<OpT>(-accA[j] * bt4[j]);
+                        sB[16 * ar * PT + 16 * ac + j * PT + oW] = from_f32<OpT>(accB[j]);
                     }
                 }
-            Frag<OpT> fR[NTB][NCT];
+            });
+        }
+        barrier_lds();
+
+        // ====== C: diagonal blocks T_aa = (I + A_aa)^{-1} on wave 0; K~, Q~ formed in place ======
+        if (wave == 0) {
+            if ((lane >> 4) < NT) {
+                // column (lane & 15) of T_aa by right-looking forward substitution; A_aa read by columns
+                const int jj = lane & 15;
+                float col[16];
 #pragma unroll
-            for (int kb = 0; kb < NTB; ++kb)
+                for (int r = 0; r < 16; ++r) col[r] = (r == jj) ? 1.0f : 0.0f;
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const bool hi = 2 * kb + 1 < NT;
-                    acc_pair_frag(fR[kb][ct], Rh[2 * kb][ct], Rh[hi ? 2 * kb + 1 : 2 * kb][ct], hi);
+                for (int i = 0; i < 15; ++i) {
+                    float acol[16];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4_t v4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sAd + oAdT + i * PD + 4 * q4);
+                        acol[4 * q4] = v4[0]; acol[4 * q4 + 1] = v4[1]; acol[4 * q4 + 2] = v4[2]; acol[4 * q4 + 3] = v4[3];
+                    }
+#pragma unroll
+                    for (int r = i + 1; r < 16; ++r) col[r] -= acol[r] * col[i];
                 }
-            f32x4_t U[NT][NCT];
 #pragma unroll
-            for (int ar = 0; ar < NT; ++ar) {
+                for (int r = 0; r < 16; ++r) sTA[oE1 + r * PT] = from_f32<OpT>(col[r]);
+            }
+        } else {
+            // K~ = Lk 2^{rho_a}, Q~ = Lq 2^{rho_a} (factors <= 1), in place
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) U[ar][ct] = zero4();
-#pragma unroll
-                for (int kb = 0; kb <= ar / 2; ++kb) {
-                    Frag<OpT> ft;
-                    lds_row_frag(ft, sT + (16 * ar + lr) * PT + 32 * kb, lg);
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) U[ar][ct] = mma(ft, fR[kb][ct], U[ar][ct]);
+            for (int arr = 0; arr < 2; ++arr) {
+                KDA_LDS OpT* base = arr ? sLq : sLk;
+                for (int m = 0; cvRow0 + m * CV_ROWS < C; ++m) {
+                    const int row = cvRow0 + m * CV_ROWS;
+                    KDA_LDS OpT* p = base + oCv + m * CV_ROWS * PK;
+                    const typename QO::raw x = QO::load(p);
+                    const f32x4_t e4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sE + (row >> 4) * DK + cvC4);
+                    QO::store(p, QO::get(x, 0) * e4[0], QO::get(x, 1) * e4[1], QO::get(x, 2) * e4[2],
+                              QO::get(x, 3) * e4[3]);
                 }
             }
+        }
+        barrier_lds();
+
+        // ================= D: state-dependent products =================
+        Frag<OpT> fs[NKB][NCT];   // S as B operand
 #pragma unroll
-            for (int kb = 0; kb < NTB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const bool hi = 2 * kb + 1 < NT;
-                    acc_pair_frag(fU[kb][ct], U[2 * kb][ct], U[hi ? 2 * kb + 1 : 2 * kb][ct], hi);
+            for (int ct = 0; ct < NCT; ++ct) acc_pair_frag(fs[kb][ct], st[2 * kb][ct], st[2 * kb + 1][ct], true);
+
+        // X = K~ S, then RHS = beta (V - X)
+        f32x4_t Rh[NT][NCT];
+#pragma unroll
+        for (int ar = 0; ar < NT; ++ar) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                Frag<OpT> fk;
+                frag_ld(fk, sLk + 16 * ar * PK + 32 * kb + oK);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = mma(fk, fs[kb][ct], Rh[ar][ct]);
+            }
+            const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sBeta + 16 * ar + 4 * lg);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float vv = zero_v ? 0.0f : to_f32<TIn>(sV[(16 * ar + j) * PV + ct * 16 + oV]);
+                    Rh[ar][ct][j] = bt4[j] * (vv - Rh[ar][ct][j]);
                 }
+            }
         }
 
-        // O = P + Bqk U
+        // U by blocked forward substitution: U_a = T_aa (RHS_a - sum_{b<a} A_ab U_b)
+        f32x4_t U[NT][NCT];
+        Frag<OpT> fU[NTB][NCT];
+#pragma unroll
+        for (int ar = 0; ar < NT; ++ar) {
+            f32x4_t W[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) W[ct] = Rh[ar][ct];
+#pragma unroll
+            for (int kb = 0; kb < ar / 2; ++kb) {
+                Frag<OpT> fa;
+                frag_ld(fa, sTA + 16 * ar * PT + 32 * kb + oT);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) W[ct] = mma(fa, fU[kb][ct], W[ct]);
+            }
+            if (ar & 1) {
+                Frag<OpT> fa;
+                frag_ld_lo(fa, sTA + 16 * ar * PT + 16 * (ar - 1) + oT);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    Frag<OpT> fb;
+                    acc_pair_frag(fb, U[ar - 1][ct], U[ar - 1][ct], false);
+                    W[ct] = mma(fa, fb, W[ct]);
+                }
+            }
+            Frag<OpT> ft;
+            frag_ld_lo(ft, sTA + 16 * ar * PT + 16 * ar + oT);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                Frag<OpT> fw;
+                acc_pair_frag(fw, W[ct], W[ct], false);
+                U[ar][ct] = mma(ft, fw, zero4());
+            }
+            if (ar & 1) {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) acc_pair_frag(fU[ar / 2][ct], U[ar - 1][ct], U[ar][ct], true);
+            } else if (ar == NT - 1) {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) acc_pair_frag(fU[ar / 2][ct], U[ar][ct], U[ar][ct], false);
+            }
+        }
+
+        // O = Q~ S + Bqk U, one 16-row tile at a time through this wave's own LDS rows
         if (has_o) {
 #pragma unroll
-            for (int ar = 0; ar < NT; ++ar)
+            for (int ar = 0; ar < NT; ++ar) {
+                f32x4_t O[NCT];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) O[ct] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    Frag<OpT> fq;
+                    frag_ld(fq, sLq + 16 * ar * PK + 32 * kb + oK);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) O[ct] = mma(fq, fs[kb][ct], O[ct]);
+                }
 #pragma unroll
                 for (int kb = 0; kb <= ar / 2; ++kb) {
                     Frag<OpT> fb;
-                    lds_row_frag(fb, sB + (16 * ar + lr) * PT + 32 * kb, lg);
+                    frag_ld(fb, sB + 16 * ar * PT + 32 * kb + oT);
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) Pq[ar][ct] = mma(fb, fU[kb][ct], Pq[ar][ct]);
+                    for (int ct = 0; ct < NCT; ++ct) O[ct] = mma(fb, fU[kb][ct], O[ct]);
                 }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sO[j * PW + ct * 16 + oOw] = from_f32<TIn>(O[ct][j]);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int m = 0; m < NOTL; ++m) {
+                    const int e = lane + 64 * m;
+                    if (NOT % 64 == 0 || e < NOT) {
+                        const int row = e / VPRW;
+                        const u32x4_t x = *reinterpret_cast<const KDA_LDS u32x4_t*>(sO + oOr + m * (64 / VPRW) * PW);
+                        if (c0 + 16 * ar + row < t_end)
+                            *reinterpret_cast<u32x4_t*>(go + (c0 + 16 * ar + m * (64 / VPRW)) * HD + oGo) = x;
+                    }
+                }
+            }
         }
 
         // S <- Diag(2^{g_C}) S + K'^T U
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const f32x4_t gam = *reinterpret_cast<const f32x4_t*>(sE + NT * DK + 16 * it + 4 * lg);
+            const f32x4_t gam = *reinterpret_cast<const KDA_LDS f32x4_t*>(sE + NT * DK + 16 * it + 4 * lg);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -507,34 +641,9 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
 #pragma unroll
             for (int kb = 0; kb < NTB; ++kb) {
                 Frag<OpT> fkp;
-                lds_row_frag(fkp, sKpT + (16 * it + lr) * PT + 32 * kb, lg);
+                frag_ld(fkp, sKpT + 16 * it * PT + 32 * kb + oT);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) st[it][ct] = mma(fkp, fU[kb][ct], st[it][ct]);
-            }
-        }
-
-        // stage O through LDS and write whole rows
-        if (has_o) {
-#pragma unroll
-            for (int ar = 0; ar < NT; ++ar)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const int wc = wave * 16 * NCT + ct * 16 + lr;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        sO[(16 * ar + 4 * lg + j) * PV + wc] = from_f32<TIn>(Pq[ar][ct][j]);
-                }
-            __syncthreads();
-#pragma unroll
-            for (int m = 0; m < NVV; ++m) {
-                const int e = tid + 256 * m;
-                if (e < NV) {
-                    const int row = e / VPR, cv = e % VPR;
-                    const long long t = c0 + row;
-                    if (t < t_end)
-                        *reinterpret_cast<uint4*>(go + t * HD + cv * VEL) =
-                            *reinterpret_cast<const uint4*>(sO + row * PV + cv * VEL);
-                }
             }
         }
     }

@@ -37,6 +37,7 @@ def assert_close(name, got, ref, dtype):
     assert np.isfinite(g).all(), f"{name}: non-finite values"
     r = rel_l2(g, ref)
     m = max_abs(g, ref)
+    print(f"    {name}: rel-L2 {r:.3e} max-abs {m:.3e} ({dtype})", flush=True)
     assert r <= rl and m <= ma, f"{name}: rel-L2 {r:.3e} (<= {rl}) max-abs {m:.3e} (<= {ma})"
     return r, m
 
