@@ -41,6 +41,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def profiled_traffic(summary, sources):
+    """HBM bytes per launch recorded in profiles/<summary> from rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    or None when the kernel sources have changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ")):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, "chunked_gated_delta_13_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if rec.get("source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def prefill_bytes(B, T, H, d, with_state=True):
     b = B * T * H * BYTES_PER_TOKEN_HEAD
     if with_state:
@@ -136,32 +160,39 @@ def bench_decode(kda, gen, steps=1000, pool=8):
     return w, wall, ev
 
 
-def cpu_baseline(gen_inputs, w, budget_s=20.0):
-    """Oracle (float64, OpenMP) on the host cores over (b=0, first Hs heads, all T tokens)."""
+def cpu_baseline(gen_inputs, w, budget_s=15.0):
+    """Oracle (float64, OpenMP) on the host cores over a bounded sample of the prefill workload:
+    the first P (sequence, head) pairs in sequence-major order, all T tokens each."""
     import oracle
     import torch
     cores = oracle.default_threads()
-    sl = lambda x: x[0:1, :, :hs].contiguous().cpu()  # noqa: E731
-    hs = 1
+
+    def gather(pairs):
+        out = []
+        for key in ("q", "k", "v", "log_alpha", "beta"):
+            x = gen_inputs[key]
+            out.append(torch.stack([x[b, :, h] for b, h in pairs], dim=1)[None].cpu())
+        s0 = torch.stack([gen_inputs["S0"][b, h] for b, h in pairs])[None].cpu()
+        return out, s0
+
+    all_pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    args, s0 = gather(all_pairs[:1])
     t0 = time.perf_counter()
-    oracle.prefill(*(sl(gen_inputs[k]) for k in ("q", "k", "v", "log_alpha", "beta")),
-                   S0=gen_inputs["S0"][0:1, :hs].cpu(), nthreads=cores)
+    oracle.prefill(*args, S0=s0, nthreads=cores)
     t1 = time.perf_counter() - t0
     # the oracle parallelises over (head, 32-column block): 4 units per head at d_v = 128
-    hs = int(max(1, min(w.H, (budget_s / max(t1, 1e-3)) * max(1, cores // 4))))
-    hs = max(1, min(w.H, hs))
-    args = [sl(gen_inputs[k]) for k in ("q", "k", "v", "log_alpha", "beta")]
-    s0 = gen_inputs["S0"][0:1, :hs].cpu()
+    n = int(min(len(all_pairs), max(1, budget_s / max(t1, 1e-3) * max(1, cores // 4))))
+    args, s0 = gather(all_pairs[:n])
     t0 = time.perf_counter()
     oracle.prefill(*args, S0=s0, nthreads=cores)
     el = time.perf_counter() - t0
-    token_heads = w.T * hs
+    token_heads = w.T * n
     tok_s = token_heads / w.H / el
-    log(f"[cpu] oracle on {hs} heads x {w.T} tokens: {el:.2f} s with {cores} threads")
+    log(f"[cpu] oracle on {n} (sequence, head) pairs x {w.T} tokens: {el:.2f} s, {cores} threads")
     del args, s0
     return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"sequence 0, heads 0..{hs-1} of {w.H}, all {w.T} tokens "
-                      f"({token_heads} token-heads, {el:.1f} s); tokens/s = token-heads/s / {w.H}"}
+            "sample": f"first {n} of {len(all_pairs)} (sequence, head) pairs, all {w.T} tokens each "
+                      f"({token_heads} token-heads in {el:.1f} s); tokens/s = token-heads/s / {w.H}"}
 
 
 def main():
@@ -174,6 +205,10 @@ def main():
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
+    ap.add_argument("--decode-only", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (known traffic) so that "
+                         "HBM byte counters can be scaled")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -188,6 +223,21 @@ def main():
         sys.exit(1)
     kda.load_library()
     torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[calibration] 3 copies of 1 GiB (1073741824 bytes read + written each)")
+        del src, dst
+    if args.decode_only:
+        wd, dwall, dev_s = bench_decode(kda, gen, args.decode_steps)
+        step_s = dev_s / args.decode_steps
+        gbs = decode_bytes(wd.N, wd.H, wd.dk) / step_s / 1e9
+        log(f"[decode] {step_s * 1e6:.1f} us per step, {gbs:.1f} GB/s")
+        return
 
     w, d, wall, ev, plan = bench_prefill(kda, gen, args.steps, args.warmup)
     tokens = w.B * w.T
@@ -215,7 +265,9 @@ def main():
                    "parallelism": "1 GPU"},
         "roofline": {"bound": "hbm", "kernel": "kda_prefill_kernel<128,2,64,bf16>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic("kda_prefill_kernel_model_width.md",
+                                                 ["kda_prefill_kernel.h", "kda_device.h"]),
                      "alg_bytes_per_launch": alg_bytes, "launch_ms": launch_s * 1e3,
                      "useful_tflops": useful_tflops,
                      "useful_frac_of_bf16_peak": useful_tflops / BF16_PEAK_TFLOPS},
@@ -233,6 +285,8 @@ def main():
                             "us_per_step": step_s * 1e6, "state_GBps": gbs,
                             "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
                             "alg_bytes_per_step": decode_bytes(wd.N, wd.H, wd.dk),
+                            "traffic": profiled_traffic("kda_decode_kernel_n256.md",
+                                                        ["kda_decode.hip", "kda_device.h"]),
                             "tokens_per_s": wd.N * args.decode_steps / dwall}
     if not args.prefill_only and not args.no_long:
         wl, lwall, lev = bench_long(kda, gen, max(2, args.steps // 5), 1)

@@ -6,8 +6,8 @@
 // "Kimi K3" (meridianbulletin.com), "Parallelizing Sequential State Updates"
 // (the tokens of a chunk are processed in parallel, then the state is handed to
 // the next chunk); "Kimi K3's architecture" (orkas.ai), "A lower bound that
-// deleted a GPU code path" (with log alpha >= -5 the accumulated log-decay of a
-// 16-token tile stays inside (-80, 0), so its reciprocal fits the 8-bit
+// deleted a GPU code path" (with log alpha >= -5, 16 tokens can decay by at
+// most e^-80 in total, so the inverse of that decay still fits the 8-bit
 // exponent of bf16 and the diagonal tiles use the same dense product as the
 // others).
 //

@@ -1,10 +1,11 @@
 // On-device prefix scan over sequence segments, and a small state copy.
 //
 // Sources: "Kimi K3" (meridianbulletin.com), "Parallelizing Sequential State
-// Updates" (the computation is split into local state increments and
-// transition matrices, and a prefix scan reconstructs the exact sequential
-// states); "Kimi K3's architecture" (orkas.ai), "The bill comes due in the
-// serving stack" (a cumulative transition and a zero-start state compose).
+// Updates" (each piece of the sequence contributes a transition and an
+// increment, and a prefix scan over the pieces recovers the same states as
+// the token-by-token run); "Kimi K3's architecture" (orkas.ai), "The bill
+// comes due in the serving stack" (the per-segment transition and the state
+// reached from zero combine exactly across segments).
 //
 // Entry state of segment s:  S_in(0) = S0,  S_in(s+1) = M_s S_in(s) + H_s.
 // State columns are independent, so a workgroup owns (head, 16 columns) and

@@ -3,11 +3,11 @@
  *
  * What is computed (per sequence b and head h; heads and sequences are
  * independent).  Sources: "Inside Kimi K3: Architecture of an Open Frontier
- * Model" (academa.ai lecture), sequence paragraph — a fixed-size state carried
- * token to token, a diagonal forget gate alpha that shrinks retained history,
- * a beta-scaled delta write that corrects what is stored, log-decay bounded
- * below at -5; "Kimi K3" (meridianbulletin.com), "Handling One Million Tokens
- * with a Fixed-Size State Matrix" (alpha clamped to [e^-5, 1]) and
+ * Model" (academa.ai lecture), sequence paragraph — one state of fixed shape passed
+ * from token to token, a per-channel diagonal decay alpha applied to it, then
+ * a beta-weighted write that corrects the stored association, with a floor of
+ * -5 on the log-decay; "Kimi K3" (meridianbulletin.com), "Handling One Million Tokens
+ * with a Fixed-Size State Matrix" (alpha limited to [e^-5, 1]) and
  * "Parallelizing Sequential State Updates" (tokens of a chunk in parallel,
  * then state hand-off; a scheduler that spreads long prefill over the compute
  * units of one card; transitions and increments joined by a prefix scan).
@@ -119,8 +119,8 @@ kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v,
  * identity with zero values) and increment H_s (from a zero state) are formed
  * first, joined by an on-device prefix scan S_in(s+1) = M_s S_in(s) + H_s, and
  * every segment is then run from its entry state.  Pages: "Kimi K3's
- * architecture", "The bill comes due in the serving stack" (a segment is a
- * cumulative transition plus a zero-start state, two quantities that compose).
+ * architecture", "The bill comes due in the serving stack" (per segment, the transition and
+ * the state reached from zero combine exactly across segments).
  * The workspace must hold kda_chunk_prefill_workspace_bytes(..., seg_len).
  */
 kda_status_t kda_chunk_prefill_ex(const void *q, const void *k, const void *v,

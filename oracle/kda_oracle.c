@@ -9,16 +9,16 @@
  *
  * What it computes (one head at a time, heads and sequences independent).
  * Sources: "Inside Kimi K3: Architecture of an Open Frontier Model"
- * (academa.ai lecture), the sequence paragraph on Kimi Delta Attention (a
- * fixed-size state carried token to token; "the first line transforms the
- * old state, the second writes the new token's correction"; the diagonal
- * alpha term is the forget gate; the beta k v term is the delta write; the
- * log-decay is bounded below at -5); "Kimi K3" (meridianbulletin.com),
- * section "Handling One Million Tokens with a Fixed-Size State Matrix" (state
- * S updated by the delta rule, beta = write strength, alpha = forgetting,
- * alpha clamped to [e^-5, 1]); "Kimi K3's architecture" (orkas.ai), section
- * "A lower bound that deleted a GPU code path" (each step keeps at least
- * 0.67% = e^-5 of what it held).
+ * (academa.ai lecture), sequence paragraph: one state of fixed shape is
+ * passed from token to token; its update has two parts, a per-channel
+ * diagonal decay (the forget gate) applied to the previous state, then a
+ * beta-weighted write that corrects the stored association; the log-decay
+ * has a floor of -5.  "Kimi K3" (meridianbulletin.com), section "Handling One
+ * Million Tokens with a Fixed-Size State Matrix": S follows the delta rule,
+ * beta sets the write strength, alpha the forgetting, and alpha is limited to
+ * the interval [e^-5, 1].  "Kimi K3's architecture" (orkas.ai), section "A
+ * lower bound that deleted a GPU code path": a single step can shrink the
+ * state to no less than e^-5, about 0.67%.
  *
  * The update formula itself is not printed on the pages (it was lost in the
  * text extraction).  The reading used here, token by token, with S a
