@@ -195,6 +195,12 @@ def cpu_baseline(gen_inputs, w, budget_s=15.0):
                       f"({token_heads} token-heads in {el:.1f} s); tokens/s = token-heads/s / {w.H}"}
 
 
+def prefill_kernel_name() -> str:
+    """Instantiation that runs the model-width workload (one 128-column slice per workgroup)."""
+    nw = 4 if os.environ.get("KDA_PREFILL_WAVES") == "4" else 8
+    return f"kda_prefill_kernel<PrefillCfg<128,{8 // nw},64,bf16,{nw}>>"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,7 +269,7 @@ def main():
                    "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
                    "tokens_per_step": tokens, "seg_len": plan[0], "n_vs": plan[1],
                    "parallelism": "1 GPU"},
-        "roofline": {"bound": "hbm", "kernel": "kda_prefill_kernel<128,2,64,bf16>",
+        "roofline": {"bound": "hbm", "kernel": prefill_kernel_name(),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": profiled_traffic("kda_prefill_kernel_model_width.md",

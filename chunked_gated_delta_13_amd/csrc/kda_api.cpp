@@ -11,8 +11,8 @@
 #include "kda_internal.h"
 
 namespace kda {
-hipError_t launch_prefill_bf16(int dk, int nct, int chunk, const PrefillArgs& a, hipStream_t s);
-hipError_t launch_prefill_f32(int dk, int nct, int chunk, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
 }  // namespace kda
 
 namespace {
@@ -20,6 +20,7 @@ namespace {
 using kda::PrefillArgs;
 
 constexpr long long kMinSegTokens = 4096;   // shortest segment worth a transition pass
+constexpr int kDefaultWaves = 8;            // waves per workgroup for 128-column bf16 slices
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -64,7 +65,7 @@ kda_status_t check_prefill_shape(int B, int T, int H, int dk, int dv, int chunk,
     if (dk <= 0 || dv <= 0 || chunk <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
     if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
-    if (!kda::prefill_supported(dk, 1, chunk, dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
+    if (!kda::prefill_supported(dk, dv, chunk, dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
     long long n = 0;
     if (!mul_ok((long long)B * T, (long long)H * dk, &n)) return KDA_ERR_INVALID_ARGUMENT;
     return KDA_OK;
@@ -99,7 +100,7 @@ kda_status_t resolve_plan(int B, int T, int H, int dk, int dv, int chunk, kda_dt
     if (seg_len_in < 0 || (seg_len_in > 0 && seg_len_in % chunk != 0)) return KDA_ERR_INVALID_ARGUMENT;
     int vs = n_vs_in > 0 ? n_vs_in : a_vs;
     if (n_vs_in < 0 || vs > 2 || (vs == 2 && dv != 128)) return KDA_ERR_INVALID_ARGUMENT;
-    if (!kda::prefill_supported(dk, (dv / vs) / 64, chunk, dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
+    if (!kda::prefill_supported(dk, dv / vs, chunk, dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
     if (sl <= 0 || sl >= T) sl = T > 0 ? T : chunk;
     long long ns = T > 0 ? ((long long)T + sl - 1) / sl : 1;
     if (ns > (1 << 20)) return KDA_ERR_UNSUPPORTED;
@@ -121,18 +122,31 @@ size_t workspace_for(int B, int H, int dk, int dv, int n_seg) {
 namespace kda {
 
 
-bool prefill_supported(int dk, int nct, int chunk, bool f32) {
-    if (nct != 1 && nct != 2) return false;
-    if (nct == 2 && dk != 128) return false;
+bool prefill_supported(int dk, int dvw, int chunk, bool f32) {
     if (dk != 64 && dk != 128) return false;
+    if (dvw != 64 && dvw != 128) return false;
+    if (dvw > dk) return false;
     if (chunk != 16 && chunk != 32 && chunk != 64) return false;
     if (f32 && chunk == 64) return false;   // fp32 operands for a 64-token chunk exceed 160 KiB of LDS
     return true;
 }
 
-hipError_t launch_prefill(int dk, int nct, int chunk, bool f32, const PrefillArgs& a, hipStream_t s) {
-    if (!prefill_supported(dk, nct, chunk, f32)) return hipErrorInvalidValue;
-    return f32 ? launch_prefill_f32(dk, nct, chunk, a, s) : launch_prefill_bf16(dk, nct, chunk, a, s);
+// Waves per workgroup for a 128-column slice in bf16: 4 (32 columns per wave) or 8 (16 columns
+// per wave, two waves per SIMD).  KDA_PREFILL_WAVES overrides the default (tuning only).
+static int prefill_waves(int dvw, bool f32) {
+    if (f32 || dvw != 128) return 4;
+    static int cached = 0;
+    if (cached == 0) {
+        const char* e = getenv("KDA_PREFILL_WAVES");
+        cached = (e && atoi(e) == 8) ? 8 : (e && atoi(e) == 4) ? 4 : kDefaultWaves;
+    }
+    return cached;
+}
+
+hipError_t launch_prefill(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a, hipStream_t s) {
+    if (!prefill_supported(dk, dvw, chunk, f32)) return hipErrorInvalidValue;
+    const int nw = prefill_waves(dvw, f32);
+    return f32 ? launch_prefill_f32(dk, dvw, nw, chunk, a, s) : launch_prefill_bf16(dk, dvw, nw, chunk, a, s);
 }
 
 }  // namespace kda
@@ -230,7 +244,7 @@ kda_status_t kda_chunk_prefill_ex(const void* q, const void* k, const void* v, c
         return KDA_OK;
     }
 
-    const int nct = (dv / vs) / 64;
+    const int dvw = dv / vs;
     const bool f32 = dt == KDA_F32;
     const long long SS = (long long)dk * dv;
 
@@ -261,7 +275,7 @@ kda_status_t kda_chunk_prefill_ex(const void* q, const void* k, const void* v, c
         a.n_seg_launch = 1;
         a.n_units = B * H;
         a.zero_values = 0;
-        if (kda::launch_prefill(dk, nct, chunk, f32, a, s) != hipSuccess) return KDA_ERR_DEVICE;
+        if (kda::launch_prefill(dk, dvw, chunk, f32, a, s) != hipSuccess) return KDA_ERR_DEVICE;
         return KDA_OK;
     }
 
@@ -284,13 +298,13 @@ kda_status_t kda_chunk_prefill_ex(const void* q, const void* k, const void* v, c
     pm.seg0 = 0;
     pm.n_seg_launch = ns - 1;
     pm.n_units = (int)(bh * (ns - 1));
-    if (kda::launch_prefill(dk, nct, chunk, f32, pm, s) != hipSuccess) return KDA_ERR_DEVICE;
+    if (kda::launch_prefill(dk, dvw, chunk, f32, pm, s) != hipSuccess) return KDA_ERR_DEVICE;
 
     PrefillArgs ph = pm;  // H_s: zero start, real values, no output
     ph.init_mode = 0;
     ph.zero_values = 0;
     ph.s_out = wsH;
-    if (kda::launch_prefill(dk, nct, chunk, f32, ph, s) != hipSuccess) return KDA_ERR_DEVICE;
+    if (kda::launch_prefill(dk, dvw, chunk, f32, ph, s) != hipSuccess) return KDA_ERR_DEVICE;
 
     kda::ScanArgs sa;
     sa.M = wsM;
@@ -315,7 +329,7 @@ kda_status_t kda_chunk_prefill_ex(const void* q, const void* k, const void* v, c
     pf.seg0 = 0;
     pf.n_seg_launch = ns;
     pf.n_units = (int)(bh * ns);
-    if (kda::launch_prefill(dk, nct, chunk, f32, pf, s) != hipSuccess) return KDA_ERR_DEVICE;
+    if (kda::launch_prefill(dk, dvw, chunk, f32, pf, s) != hipSuccess) return KDA_ERR_DEVICE;
     return KDA_OK;
 }
 

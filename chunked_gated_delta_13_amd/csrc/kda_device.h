@@ -163,6 +163,26 @@ __device__ __forceinline__ void lds_store_run(KDA_LDS float* p, const float (&v)
 // A lane-dependent value pinned in a register: the compiler may not recompute
 // it where it is used (inside the chunk loop that would reintroduce runtime
 // multiplies into LDS addressing).
+// p advanced by a 32-bit byte offset: with p uniform this is the scalar-base + vector-offset
+// address form, one register per lane instead of a 64-bit pointer.
+template <typename T> __device__ __forceinline__ T* at_byte(T* p, uint32_t off) {
+    return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + off);
+}
+template <typename T> __device__ __forceinline__ const T* at_byte(const T* p, uint32_t off) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + off);
+}
+
+// An opaque copy of a lane offset, taken where the address is formed: keeps the compiler from
+// hoisting "uniform base + offset" out of a loop as a 64-bit per-lane pointer.
+__device__ __forceinline__ uint32_t pinned_u(uint32_t x) { asm volatile("" : "+v"(x)); return x; }
+// An opaque copy of an LDS address: the compiler keeps it in one register and reaches nearby
+// elements through the instruction's immediate offset instead of materialising one address
+// register per constant offset.
+template <typename T> __device__ __forceinline__ KDA_LDS T* lds_pin(KDA_LDS T* p) {
+    uint32_t x = (uint32_t)(size_t)p;
+    asm volatile("" : "+v"(x));
+    return (KDA_LDS T*)(size_t)x;
+}
 __device__ __forceinline__ int pinned(int x) {
     asm volatile("" : "+v"(x));
     return x;

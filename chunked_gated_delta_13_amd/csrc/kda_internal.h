@@ -56,8 +56,9 @@ struct DecodeArgs {
     long long NH;
 };
 
-bool prefill_supported(int dk, int nct, int chunk, bool f32);
-hipError_t launch_prefill(int dk, int nct, int chunk, bool f32, const PrefillArgs& a,
+// dvw = state columns per workgroup (d_v / column slices).
+bool prefill_supported(int dk, int dvw, int chunk, bool f32);
+hipError_t launch_prefill(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a,
                           hipStream_t stream);
 hipError_t launch_scan(int dk, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_decode(int dk, bool f32, const DecodeArgs& a, hipStream_t stream);

@@ -3,19 +3,20 @@
 
 namespace kda {
 
-hipError_t launch_prefill_f32(int dk, int nct, int chunk, const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_prefill_f32(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s) {
     using T = float;
-    if (dk == 128 && nct == 2) {
-        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<128, 2, 32, T>>(a, s);
-        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<128, 2, 16, T>>(a, s);
+    if (nw != 4) return hipErrorInvalidValue;
+    if (dk == 128 && dvw == 128) {
+        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<128, 2, 32, T, 4>>(a, s);
+        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<128, 2, 16, T, 4>>(a, s);
     }
-    if (dk == 128 && nct == 1) {
-        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<128, 1, 32, T>>(a, s);
-        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<128, 1, 16, T>>(a, s);
+    if (dk == 128 && dvw == 64) {
+        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<128, 1, 32, T, 4>>(a, s);
+        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<128, 1, 16, T, 4>>(a, s);
     }
-    if (dk == 64 && nct == 1) {
-        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<64, 1, 32, T>>(a, s);
-        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<64, 1, 16, T>>(a, s);
+    if (dk == 64 && dvw == 64) {
+        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<64, 1, 32, T, 4>>(a, s);
+        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<64, 1, 16, T, 4>>(a, s);
     }
     return hipErrorInvalidValue;
 }

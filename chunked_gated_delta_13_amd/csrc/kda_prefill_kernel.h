@@ -1,8 +1,9 @@
 // Fused chunked KDA prefill kernel for gfx950.
 //
-// One workgroup of 256 threads (4 wave64s) owns one unit = (sequence b, head h,
+// One workgroup of NW wave64s (4 or 8) owns one unit = (sequence b, head h,
 // segment s, state-column slice) and walks the unit's chunks of C tokens in
-// order, carrying the fp32 state slice S (DK x 64*NCT) in registers.  Sources:
+// order, carrying the fp32 state slice S (DK x 16*NCT*NW) in registers, 16*NCT
+// columns per wave.  Sources:
 // "Kimi K3" (meridianbulletin.com), "Parallelizing Sequential State Updates"
 // (the tokens of a chunk are processed in parallel, then the state is handed to
 // the next chunk); "Kimi K3's architecture" (orkas.ai), "A lower bound that
@@ -37,20 +38,24 @@
 
 namespace kda {
 
-template <int DK_, int NCT_, int C_, typename TIn_>
+template <int DK_, int NCT_, int C_, typename TIn_, int NW_ = 4>
 struct PrefillCfg {
     static constexpr int DK = DK_;
     static constexpr int NCT = NCT_;             // 16-column tiles per wave
+    static constexpr int NW = NW_;               // waves per workgroup
+    static constexpr int NTH = 64 * NW_;         // threads per workgroup
     static constexpr int C = C_;
     using TIn = TIn_;
     using OpT = TIn_;                            // matrix-core operand type
     static constexpr int NT = C / 16;            // 16-token row tiles per chunk
     static constexpr int NTB = (NT + 1) / 2;     // 32-token contraction blocks per chunk
-    static constexpr int DVW = 64 * NCT;         // state columns per workgroup
+    static constexpr int DVW = 16 * NCT * NW;    // state columns per workgroup
     static constexpr int NQ = DK / 4;            // channel quads (decay phase)
-    static constexpr int NSEG = 256 / NQ;        // token segments (decay phase)
+    static constexpr int NSEG = NTH / NQ;        // token segments (decay phase)
     static constexpr int TPS = C / NSEG;         // tokens per segment
-    static constexpr int SPT = 16 / TPS;         // segments per 16-token tile
+    static constexpr int G = C / 16;             // tokens per decay group (16 groups per chunk)
+    static constexpr int GPT = TPS / G;          // decay groups per segment
+    static constexpr int SPT = 16 / G;           // decay groups per 16-token tile
     static constexpr int CP = C < 32 ? 32 : C;   // token extent of token-indexed rows
     static constexpr int PADE = sizeof(OpT) == 2 ? 8 : 4;
     static constexpr int PK = DK + PADE;         // pitch of [C][DK] operand arrays
@@ -62,7 +67,7 @@ struct PrefillCfg {
     static constexpr int VEL = 16 / (int)sizeof(TIn);           // elements per 16-byte vector
     static constexpr int VPR = DVW / VEL;                       // vectors per value row
     static constexpr int NV = C * VPR;                          // vectors per value chunk
-    static constexpr int NVV = (NV + 255) / 256;                // vectors per thread
+    static constexpr int NVV = (NV + NTH - 1) / NTH;            // vectors per thread
     static constexpr int VPRW = 16 * NCT / VEL;                 // vectors per wave output row
     static constexpr int NOT = 16 * VPRW;                       // vectors per wave output tile
     static constexpr int NOTL = (NOT + 63) / 64;                // per lane
@@ -70,8 +75,12 @@ struct PrefillCfg {
     static constexpr int NQT = C * DK / 4;                      // quads per [C][DK] array
 
     static_assert(TPS >= 1 && 16 % TPS == 0, "segment must sit inside one tile");
+    static_assert(TPS % G == 0, "segment holds whole decay groups");
     static_assert(DK % 32 == 0 && C % 16 == 0 && NT <= 4, "shape");
-    static_assert(NDMA % 4 == 0, "log-decay loads split evenly over the 4 waves");
+    static_assert(NDMA % NW == 0, "log-decay loads split evenly over the waves");
+    static_assert(NTH % VPR == 0, "value rows split evenly over the threads");
+    static constexpr int CV_ROWS = (NTH - 64) / (DK / 4);       // rows per in-place scaling step
+    static_assert((NTH - 64) % (DK / 4) == 0, "in-place scaling covers whole rows");
 
     static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t oLq = 0;
@@ -86,8 +95,8 @@ struct PrefillCfg {
     static constexpr size_t oD = oE + al(4 * (NT + 1) * DK);
     static constexpr size_t oBeta = oD + al(4 * NT * DK);
     static constexpr size_t oTot = oBeta + al(4 * C);
-    static constexpr size_t oO = oTot + al(4 * NSEG * DK);
-    static constexpr size_t LDS = oO + al(sizeof(TIn) * 4 * 16 * PW);
+    static constexpr size_t oO = oTot + al(4 * 16 * DK);
+    static constexpr size_t LDS = oO + al(sizeof(TIn) * NW * 16 * PW);
     static_assert(LDS + 4 * C * DK <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 
@@ -125,17 +134,17 @@ template <> struct Quad<float> {
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs a) {
     using TIn = typename Cfg::TIn;
     using OpT = typename Cfg::OpT;
     using QI = Quad<TIn>;
     using QO = Quad<OpT>;
     constexpr int DK = Cfg::DK, C = Cfg::C, NT = Cfg::NT, NTB = Cfg::NTB, NCT = Cfg::NCT;
     constexpr int DVW = Cfg::DVW, NQ = Cfg::NQ, NSEG = Cfg::NSEG, TPS = Cfg::TPS;
-    constexpr int SPT = Cfg::SPT, PK = Cfg::PK, PT = Cfg::PT, PV = Cfg::PV, PW = Cfg::PW;
+    constexpr int SPT = Cfg::SPT, G = Cfg::G, GPT = Cfg::GPT, PK = Cfg::PK, PT = Cfg::PT, PV = Cfg::PV, PW = Cfg::PW;
     constexpr int PD = Cfg::PD, PDB = Cfg::PDB, VEL = Cfg::VEL, VPR = Cfg::VPR, NV = Cfg::NV, NVV = Cfg::NVV;
     constexpr int VPRW = Cfg::VPRW, NOT = Cfg::NOT, NOTL = Cfg::NOTL, NDMA = Cfg::NDMA;
-    constexpr int NQT = Cfg::NQT;
+    constexpr int NQT = Cfg::NQT, NW = Cfg::NW, NTH = Cfg::NTH, CV_ROWS = Cfg::CV_ROWS;
     constexpr int NIT = DK / 16;   // 16-row tiles of the state
     constexpr int NKB = DK / 32;   // 32-channel contraction blocks
 
@@ -214,46 +223,61 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
     }
 
     // ---- zero the token-padded operand arrays once (parts never written stay zero) ----
-    for (int e = tid; e < C * PT; e += 256) {
+    for (int e = tid; e < C * PT; e += NTH) {
         sTA[e] = from_f32<OpT>(0.0f);
         sB[e] = from_f32<OpT>(0.0f);
     }
-    for (int e = tid; e < DK * PT; e += 256) sKpT[e] = from_f32<OpT>(0.0f);
+    for (int e = tid; e < DK * PT; e += NTH) sKpT[e] = from_f32<OpT>(0.0f);
 
     // ---- decay-phase thread mapping: channel quad cq, token segment sg ----
     const int cq = tid % NQ;
     const int sg = tid / NQ;
     const int ch0 = 4 * cq;
 
-    // ---- lane-dependent LDS offsets (elements), computed once: the chunk loop adds only constants ----
-    const int oA = pinned(sg * TPS * PK + ch0);                   // this thread's rows of [C][PK] arrays
-    const int oKp = pinned(ch0 * PT + sg * TPS);                  // this thread's K'^T entries
-    const int oLam = pinned(sg * TPS * DK + ch0);                 // this thread's raw log-decay
-    const int oVc = pinned((tid / VPR) * PV + (tid % VPR) * VEL); // value commit
-    const int oK = pinned(lr * PK + 4 * lg);                      // fragment row, [*][PK] arrays
-    const int oT = pinned(lr * PT + 4 * lg);                      // fragment row, [*][PT] arrays
-    const int oW = pinned(4 * lg * PT + lr);                      // accumulator element, [*][PT] arrays
-    const int oAd = pinned(lr * PD + 4 * lg);                     // transposed diagonal-block store
-    const int oAdT = pinned((lane >> 4) * PDB);                   // diagonal block of this lane (wave 0)
-    const int oE1 = pinned((lane >> 4) * 16 * (PT + 1) + (lane & 15));  // T_aa column of this lane (wave 0)
-    const int oV = pinned(4 * lg * PV + wave * 16 * NCT + lr);    // value in accumulator layout
-    const int oOw = pinned(wave * 16 * PW + 4 * lg * PW + lr);    // output staging write
-    const int oOr = pinned(wave * 16 * PW + (lane / VPRW) * PW + (lane % VPRW) * VEL);  // staging read
-    const int tq = tid - 64;                                      // waves 1..3: in-place operand scaling
-    const int oCv = pinned((tq / (DK / 4)) * PK + 4 * (tq % (DK / 4)));
+    // ---- lane-dependent LDS bases, computed once and kept opaque: every access in the chunk loop
+    //      is one of these registers plus an immediate offset (arrays grouped so that the
+    //      immediates stay below 64 KiB) ----
+    constexpr int eLk = (int)((Cfg::oLk - Cfg::oLq) / sizeof(OpT));   // element distances
+    constexpr int eKd = (int)((Cfg::oKd - Cfg::oLq) / sizeof(OpT));
+    constexpr int eTA = (int)((Cfg::oTA - Cfg::oKpT) / sizeof(OpT));
+    constexpr int eB = (int)((Cfg::oB - Cfg::oKpT) / sizeof(OpT));
+    constexpr int eBw = (int)((Cfg::oB - Cfg::oTA) / sizeof(OpT));
+    constexpr int fD = (int)((Cfg::oD - Cfg::oE) / 4);
+    constexpr int fBeta = (int)((Cfg::oBeta - Cfg::oE) / 4);
+    static_assert(Cfg::oB + sizeof(OpT) * C * PT - Cfg::oKpT < 65536, "immediate offsets");
+    static_assert(Cfg::oKd + sizeof(OpT) * C * PK - Cfg::oLq < 65536, "immediate offsets");
+    KDA_LDS OpT* const pA = lds_pin(sLq + sg * TPS * PK + ch0);      // decay-phase rows of Lq, Lk, Kd
+    KDA_LDS OpT* const pKp = lds_pin(sKpT + ch0 * PT + sg * TPS);     // this thread's K'^T entries
+    KDA_LDS float* const pLam = lds_pin(sLam + sg * TPS * DK + ch0);  // this thread's raw log-decay
+    KDA_LDS float* const pTotW = lds_pin(sTot + sg * GPT * DK + ch0); // this segment's decay-group totals
+    KDA_LDS float* const pTotR = lds_pin(sTot + ch0);                 // all segments' totals
+    KDA_LDS float* const pCh = lds_pin(sE + ch0);                     // sE, sD rows of this thread's quad
+    KDA_LDS TIn* const pVc = lds_pin(sV + (tid / VPR) * PV + (tid % VPR) * VEL);  // value commit
+    KDA_LDS OpT* const pK = lds_pin(sLq + lr * PK + 4 * lg);          // fragment rows of Lq, Lk, Kd
+    KDA_LDS OpT* const pT = lds_pin(sKpT + lr * PT + 4 * lg);         // fragment rows of KpT, TA, B
+    KDA_LDS float* const pG = lds_pin(sE + 4 * lg);                   // sE, sD, sBeta by accumulator row
+    KDA_LDS OpT* const pW = lds_pin(sTA + 4 * lg * PT + lr);          // accumulator element of TA, B
+    KDA_LDS float* const pAd = lds_pin(sAd + lr * PD + 4 * lg);       // transposed diagonal-block store
+    KDA_LDS float* const pAdT = lds_pin(sAd + (lane >> 4) * PDB);     // diagonal block of this lane (wave 0)
+    KDA_LDS OpT* const pE1 = lds_pin(sTA + (lane >> 4) * 16 * (PT + 1) + (lane & 15));  // T_aa column (wave 0)
+    KDA_LDS TIn* const pV = lds_pin(sV + 4 * lg * PV + wave * 16 * NCT + lr);  // value in accumulator layout
+    KDA_LDS TIn* const pOw = lds_pin(sO + wave * 16 * PW + 4 * lg * PW + lr);  // output staging write
+    KDA_LDS TIn* const pOr = lds_pin(sO + wave * 16 * PW + (lane / VPRW) * PW + (lane % VPRW) * VEL);
+    const int tq = tid - 64;                                          // waves 1..NW-1: in-place scaling
     const int cvRow0 = tq / (DK / 4);
-    const int cvC4 = 4 * (tq % (DK / 4));
-    constexpr int CV_ROWS = 192 / (DK / 4);                       // rows advanced per step
-    const long long oGo = (long long)(lane / VPRW) * HD + wave * 16 * NCT + (lane % VPRW) * VEL;
+    KDA_LDS OpT* const pCv = lds_pin(sLq + cvRow0 * PK + 4 * (tq % (DK / 4)));
+    KDA_LDS float* const pCe = lds_pin(sE + 4 * (tq % (DK / 4)));
+    // byte offset of this lane's output vector from the uniform row base
+    const uint32_t boGo = (uint32_t)(((lane / VPRW) * HD + wave * 16 * NCT + (lane % VPRW) * VEL) * sizeof(TIn));
 
-    // ---- per-lane global bases: inside the loop only a uniform (c0 + const) * stride is added ----
-    const TIn* gq_l = gq + (long long)(sg * TPS) * HD + ch0;
-    const TIn* gk_l = gk + (long long)(sg * TPS) * HD + ch0;
-    const float* gb_l = gbeta + (long long)(tid % C) * a.H;
+    // ---- per-lane 32-bit byte offsets: inside the loop every global address is a uniform
+    //      (scalar) row base plus one of these, so each lane keeps one register per stream ----
+    const uint32_t boQK = (uint32_t)(((sg * TPS) * HD + ch0) * sizeof(TIn));
+    const uint32_t boB = (uint32_t)((tid % C) * a.H * sizeof(float));
     const int v_row = tid / VPR, v_off = (tid % VPR) * VEL;
-    const TIn* gv_l = gv + (long long)v_row * HD + v_off;
+    const uint32_t boV = (uint32_t)((v_row * HD + v_off) * sizeof(TIn));
     const int d_row = (4 * lane) / DK, d_col = (4 * lane) % DK;   // this lane's 16 bytes of a 1 KiB block
-    const float* gla_l = gla + (long long)d_row * HD + d_col;
+    const uint32_t boLa = (uint32_t)((d_row * HD + d_col) * sizeof(float));
     constexpr int D_ROWS = 256 / DK;                               // rows per 1 KiB block
 
     // ---- prefetch of the next chunk: log-decay straight into LDS, the rest into registers ----
@@ -268,14 +292,14 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
     auto load_decay = [&](long long c0) {
         if (c0 + C <= t_end) {
 #pragma unroll
-            for (int m = 0; m < NDMA / 4; ++m) {
-                const int gi = wave * (NDMA / 4) + m;
-                lds_dma16(gla_l + (c0 + gi * D_ROWS) * HD, (KDA_LDS void*)(sLam + gi * 256));
+            for (int m = 0; m < NDMA / NW; ++m) {
+                const int gi = wave * (NDMA / NW) + m;
+                lds_dma16(at_byte(gla + (c0 + gi * D_ROWS) * HD, pinned_u(boLa)), (KDA_LDS void*)(sLam + gi * 256));
             }
         } else {
 #pragma unroll
-            for (int m = 0; m < NDMA / 4; ++m) {
-                const int gi = wave * (NDMA / 4) + m;
+            for (int m = 0; m < NDMA / NW; ++m) {
+                const int gi = wave * (NDMA / NW) + m;
                 lds_dma16(gla + clampt(c0 + gi * D_ROWS + d_row) * HD + d_col, (KDA_LDS void*)(sLam + gi * 256));
             }
         }
@@ -284,16 +308,16 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
         if (c0 + C <= t_end) {
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
-                pq[i] = QI::load(gq_l + (c0 + i) * HD);
-                pk[i] = QI::load(gk_l + (c0 + i) * HD);
+                pq[i] = QI::load(at_byte(gq + (c0 + i) * HD, pinned_u(boQK)));
+                pk[i] = QI::load(at_byte(gk + (c0 + i) * HD, pinned_u(boQK)));
             }
-            pbeta = gb_l[c0 * a.H];
-            if (!zero_v) {
+            pbeta = *at_byte(gbeta + c0 * a.H, pinned_u(boB));
+            // values are fetched even when a pass ignores them: a conditional load would make the
+            // compiler wait for it where the two paths merge
 #pragma unroll
-                for (int m = 0; m < NVV; ++m)
-                    if (NV % 256 == 0 || tid + 256 * m < NV)
-                        pv[m] = *reinterpret_cast<const u32x4_t*>(gv_l + (c0 + m * (256 / VPR)) * HD);
-            }
+            for (int m = 0; m < NVV; ++m)
+                if (NV % NTH == 0 || tid + NTH * m < NV)
+                    pv[m] = *reinterpret_cast<const u32x4_t*>(at_byte(gv + (c0 + m * (NTH / VPR)) * HD, pinned_u(boV)));
         } else {
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
@@ -302,12 +326,10 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
                 pk[i] = QI::load(gk + off);
             }
             pbeta = gbeta[clampt(c0 + (tid % C)) * a.H];
-            if (!zero_v) {
 #pragma unroll
-                for (int m = 0; m < NVV; ++m)
-                    if (NV % 256 == 0 || tid + 256 * m < NV)
-                        pv[m] = *reinterpret_cast<const u32x4_t*>(gv + clampt(c0 + v_row + m * (256 / VPR)) * HD + v_off);
-            }
+            for (int m = 0; m < NVV; ++m)
+                if (NV % NTH == 0 || tid + NTH * m < NV)
+                    pv[m] = *reinterpret_cast<const u32x4_t*>(gv + clampt(c0 + v_row + m * (NTH / VPR)) * HD + v_off);
         }
     };
 
@@ -325,11 +347,11 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
         // ================= A: commit prefetched values, per-segment cumulative decay =================
 #pragma unroll
         for (int m = 0; m < NVV; ++m) {
-            const int e = tid + 256 * m;
-            if (NV % 256 == 0 || e < NV) {
+            const int e = tid + NTH * m;
+            if (NV % NTH == 0 || e < NV) {
                 const bool ok = !zero_v && c0 + e / VPR < t_end;
                 const u32x4_t x = pv[m];
-                *reinterpret_cast<KDA_LDS u32x4_t*>(sV + oVc + m * (256 / VPR) * PV) =
+                *reinterpret_cast<KDA_LDS u32x4_t*>(pVc + m * (NTH / VPR) * PV) =
                     u32x4_t{ok ? x[0] : 0u, ok ? x[1] : 0u, ok ? x[2] : 0u, ok ? x[3] : 0u};
             }
         }
@@ -338,19 +360,22 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
         bool okt[TPS];
 #pragma unroll
         for (int i = 0; i < TPS; ++i) okt[i] = c0 + sg * TPS + i < t_end;
+        // log2-decay summed from the start of the token's decay group (G tokens); group totals to LDS
         float g[TPS][4];
         {
             float run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
-                const f32x4_t l4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sLam + oLam + i * DK);
+                const f32x4_t l4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pLam + i * DK);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    run[u] += okt[i] ? fminf(fmaxf(l4[u], kLogAlphaMin), 0.0f) * kLog2e : 0.0f;
+                    const float l2 = okt[i] ? fminf(fmaxf(l4[u], kLogAlphaMin), 0.0f) * kLog2e : 0.0f;
+                    run[u] = (i % G == 0) ? l2 : run[u] + l2;
                     g[i][u] = run[u];
                 }
+                if (i % G == G - 1)
+                    *reinterpret_cast<KDA_LDS f32x4_t*>(pTotW + (i / G) * DK) = f32x4_t{run[0], run[1], run[2], run[3]};
             }
-            *reinterpret_cast<KDA_LDS f32x4_t*>(sTot + sg * DK + ch0) = f32x4_t{run[0], run[1], run[2], run[3]};
         }
         barrier_lds();
         // the raw log-decay of this chunk is consumed: fetch the next chunk's behind everything below
@@ -358,26 +383,58 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
 
         // ================= A': references and decay-scaled operands =================
         {
-            // prefix over segments, summed in the same order by every thread
-            f32x4_t P[NSEG + 1];
-            P[0] = zero4();
+            // One summation order for every thread layout: group totals in order inside each
+            // 16-token tile, tile totals in order across the chunk.  Rt[a] = rho_a.
+            f32x4_t Rt[NT + 1];
+            Rt[0] = zero4();
 #pragma unroll
-            for (int q2 = 0; q2 < NSEG; ++q2)
-                P[q2 + 1] = P[q2] + *reinterpret_cast<const KDA_LDS f32x4_t*>(sTot + q2 * DK + ch0);
-            const int at = (sg * TPS) / 16;       // this segment's row tile
-            f32x4_t off = zero4(), rho = zero4(), nx = zero4();
+            for (int a2 = 0; a2 < NT; ++a2) {
+                f32x4_t tt = *reinterpret_cast<const KDA_LDS f32x4_t*>(pTotR + a2 * SPT * DK);
 #pragma unroll
-            for (int q2 = 0; q2 <= NSEG; ++q2) {
-                if (q2 == sg) off = P[q2];
-                if (q2 == at * SPT) rho = P[q2];
-                if (q2 == (at + 1) * SPT) nx = P[q2];
+                for (int j = 1; j < SPT; ++j) tt = tt + *reinterpret_cast<const KDA_LDS f32x4_t*>(pTotR + (a2 * SPT + j) * DK);
+                Rt[a2 + 1] = Rt[a2] + tt;
             }
-            const f32x4_t gC = P[NSEG];
+            const int at = (sg * TPS) / 16;       // this segment's row tile
+            const int jg0 = (sg * GPT) % SPT;     // its first decay group inside the tile
+            // gp[m] = sum of the tile's group totals before own group m, in the same order as above
+            f32x4_t gp[GPT];
+            {
+                const KDA_LDS float* tb = pTotR + at * SPT * DK;
+                f32x4_t run = zero4();
+#pragma unroll
+                for (int j = 0; j < SPT; ++j) {
+#pragma unroll
+                    for (int m = 0; m < GPT; ++m)
+                        if (j == jg0 + m) gp[m] = run;
+                    if (j + 1 < SPT) run = run + *reinterpret_cast<const KDA_LDS f32x4_t*>(tb + j * DK);
+                }
+            }
+            f32x4_t rho = Rt[0], nx = Rt[1];
+#pragma unroll
+            for (int a2 = 1; a2 < NT; ++a2)
+                if (at == a2) {
+                    rho = Rt[a2];
+                    nx = Rt[a2 + 1];
+                }
+            const f32x4_t gC = Rt[NT];
             float fd[4], fc[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 fd[u] = fast_exp2(nx[u] - rho[u]);   // 2^{rho_{a+1} - rho_a} in [2^-115.4, 1]
                 fc[u] = fast_exp2(gC[u] - nx[u]);    // 2^{g_C - rho_{a+1}} in (0, 1]
+            }
+            if (sg == 0) {
+#pragma unroll
+                for (int t2 = 0; t2 <= NT; ++t2) {
+                    f32x4_t e4, d4;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        e4[u] = fast_exp2(Rt[t2][u]);
+                        d4[u] = t2 < NT ? fast_exp2(Rt[t2 + 1][u] - Rt[t2][u]) : 0.0f;
+                    }
+                    *reinterpret_cast<KDA_LDS f32x4_t*>(pCh + t2 * DK) = e4;
+                    if (t2 < NT) *reinterpret_cast<KDA_LDS f32x4_t*>(pCh + fD + t2 * DK) = d4;
+                }
             }
             float kp[4][TPS];   // K' of this thread's channels, by channel: one vector store each
 #pragma unroll
@@ -385,9 +442,9 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
                 float lq[4], lk[4], kd[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float gg = g[i][u] + off[u];
-                    const float x = fast_exp2(gg - rho[u]);  // <= 1
-                    const float y = fast_exp2(rho[u] - gg);  // >= 1, at most 2^115.4 = e^80
+                    const float loc = gp[i / G][u] + g[i][u];   // g - rho_a, in [-115.4, 0]
+                    const float x = fast_exp2(loc);              // <= 1
+                    const float y = fast_exp2(-loc);             // >= 1, at most 2^115.4 = e^80
                     const float qv = okt[i] ? QI::get(pq[i], u) : 0.0f;
                     const float kv = okt[i] ? QI::get(pk[i], u) : 0.0f;
                     lq[u] = qv * x;
@@ -396,25 +453,12 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
                     // K' = k 2^{g_C - g}: the factor above 1 meets only a factor that cannot underflow
                     kp[u][i] = kv * ((y * fd[u]) * fc[u]);
                 }
-                QO::store(sLq + oA + i * PK, lq[0], lq[1], lq[2], lq[3]);
-                QO::store(sLk + oA + i * PK, lk[0], lk[1], lk[2], lk[3]);
-                QO::store(sKd + oA + i * PK, kd[0], kd[1], kd[2], kd[3]);
+                QO::store(pA + i * PK, lq[0], lq[1], lq[2], lq[3]);
+                QO::store(pA + eLk + i * PK, lk[0], lk[1], lk[2], lk[3]);
+                QO::store(pA + eKd + i * PK, kd[0], kd[1], kd[2], kd[3]);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) lds_store_run<TPS>(sKpT + oKp + u * PT, kp[u]);
-            if (sg == 0) {
-#pragma unroll
-                for (int t2 = 0; t2 <= NT; ++t2) {
-                    f32x4_t e4, d4;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        e4[u] = fast_exp2(P[t2 * SPT][u]);
-                        d4[u] = t2 < NT ? fast_exp2(P[(t2 + 1) * SPT][u] - P[t2 * SPT][u]) : 0.0f;
-                    }
-                    *reinterpret_cast<KDA_LDS f32x4_t*>(sE + t2 * DK + ch0) = e4;
-                    if (t2 < NT) *reinterpret_cast<KDA_LDS f32x4_t*>(sD + t2 * DK + ch0) = d4;
-                }
-            }
+            for (int u = 0; u < 4; ++u) lds_store_run<TPS>(pKp + u * PT, kp[u]);
         }
         // the raw q, k, v of this chunk are consumed: fetch the next chunk's
         if (c + 1 < nchunks) load_rest(c0 + C);
@@ -427,14 +471,14 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
                 constexpr int pi = decltype(PIc)::value;
                 constexpr int ar = pair_row(pi);
                 constexpr int ac = pi - ar * (ar + 1) / 2;
-                if (pi % 4 != wave) return;   // wave-uniform
+                if (pi % NW != wave) return;   // wave-uniform
                 f32x4_t accA = zero4(), accB = zero4();
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     Frag<OpT> fk, fq, fr;
-                    frag_ld(fk, sLk + 16 * ar * PK + 32 * kb + oK);
-                    frag_ld(fq, sLq + 16 * ar * PK + 32 * kb + oK);
-                    frag_ld(fr, sKd + 16 * ac * PK + 32 * kb + oK);
+                    frag_ld(fk, pK + eLk + 16 * ar * PK + 32 * kb);
+                    frag_ld(fq, pK + 16 * ar * PK + 32 * kb);
+                    frag_ld(fr, pK + eKd + 16 * ac * PK + 32 * kb);
                     if constexpr (ac < ar) {
                         // R = Kd 2^{rho_ar - rho_ac}: multiply by 2^{rho_{m+1} - rho_m} one tile at a
                         // time, the first step bringing Kd (up to 2^115) down to at most 1
@@ -444,7 +488,7 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
 #pragma unroll
                         for (int m = ac; m < ar; ++m) {
                             float d8[8];
-                            f32x8_ld(d8, sD + m * DK + 32 * kb + 4 * lg);
+                            f32x8_ld(d8, pG + fD + m * DK + 32 * kb);
 #pragma unroll
                             for (int j = 0; j < 8; ++j) val[j] *= d8[j];
                         }
@@ -454,21 +498,21 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
                     accA = mma(fk, fr, accA);
                     accB = mma(fq, fr, accB);
                 }
-                const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sBeta + 16 * ar + 4 * lg);
+                const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pG + fBeta + 16 * ar);
                 if constexpr (ac == ar) {
                     f32x4_t ad;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int rl = 4 * lg + j;
                         ad[j] = (lr < rl) ? accA[j] * bt4[j] : 0.0f;
-                        sB[16 * ar * PT + 16 * ac + j * PT + oW] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
+                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
                     }
-                    *reinterpret_cast<KDA_LDS f32x4_t*>(sAd + ar * PDB + oAd) = ad;  // transposed
+                    *reinterpret_cast<KDA_LDS f32x4_t*>(pAd + ar * PDB) = ad;  // transposed
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        sTA[16 * ar * PT + 16 * ac + j * PT + oW] = from_f32<OpT>(-accA[j] * bt4[j]);
-                        sB[16 * ar * PT + 16 * ac + j * PT + oW] = from_f32<OpT>(accB[j]);
+                        pW[16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(-accA[j] * bt4[j]);
+                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(accB[j]);
                     }
                 }
             });
@@ -488,25 +532,27 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
                     float acol[16];
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x4_t v4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sAd + oAdT + i * PD + 4 * q4);
+                        const f32x4_t v4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pAdT + i * PD + 4 * q4);
                         acol[4 * q4] = v4[0]; acol[4 * q4 + 1] = v4[1]; acol[4 * q4 + 2] = v4[2]; acol[4 * q4 + 3] = v4[3];
                     }
 #pragma unroll
                     for (int r = i + 1; r < 16; ++r) col[r] -= acol[r] * col[i];
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sTA[oE1 + r * PT] = from_f32<OpT>(col[r]);
+                for (int r = 0; r < 16; ++r) pE1[r * PT] = from_f32<OpT>(col[r]);
             }
         } else {
             // K~ = Lk 2^{rho_a}, Q~ = Lq 2^{rho_a} (factors <= 1), in place
 #pragma unroll
             for (int arr = 0; arr < 2; ++arr) {
-                KDA_LDS OpT* base = arr ? sLq : sLk;
-                for (int m = 0; cvRow0 + m * CV_ROWS < C; ++m) {
+                KDA_LDS OpT* base = arr ? pCv : pCv + eLk;
+#pragma unroll
+                for (int m = 0; m < (C + CV_ROWS - 1) / CV_ROWS; ++m) {
                     const int row = cvRow0 + m * CV_ROWS;
-                    KDA_LDS OpT* p = base + oCv + m * CV_ROWS * PK;
+                    if (row >= C) break;
+                    KDA_LDS OpT* p = base + m * CV_ROWS * PK;
                     const typename QO::raw x = QO::load(p);
-                    const f32x4_t e4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sE + (row >> 4) * DK + cvC4);
+                    const f32x4_t e4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pCe + (row >> 4) * DK);
                     QO::store(p, QO::get(x, 0) * e4[0], QO::get(x, 1) * e4[1], QO::get(x, 2) * e4[2],
                               QO::get(x, 3) * e4[3]);
                 }
@@ -530,16 +576,16 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 Frag<OpT> fk;
-                frag_ld(fk, sLk + 16 * ar * PK + 32 * kb + oK);
+                frag_ld(fk, pK + eLk + 16 * ar * PK + 32 * kb);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = mma(fk, fs[kb][ct], Rh[ar][ct]);
             }
-            const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sBeta + 16 * ar + 4 * lg);
+            const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pG + fBeta + 16 * ar);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float vv = zero_v ? 0.0f : to_f32<TIn>(sV[(16 * ar + j) * PV + ct * 16 + oV]);
+                    const float vv = zero_v ? 0.0f : to_f32<TIn>(pV[(16 * ar + j) * PV + ct * 16]);
                     Rh[ar][ct][j] = bt4[j] * (vv - Rh[ar][ct][j]);
                 }
             }
@@ -556,13 +602,13 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
 #pragma unroll
             for (int kb = 0; kb < ar / 2; ++kb) {
                 Frag<OpT> fa;
-                frag_ld(fa, sTA + 16 * ar * PT + 32 * kb + oT);
+                frag_ld(fa, pT + eTA + 16 * ar * PT + 32 * kb);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) W[ct] = mma(fa, fU[kb][ct], W[ct]);
             }
             if (ar & 1) {
                 Frag<OpT> fa;
-                frag_ld_lo(fa, sTA + 16 * ar * PT + 16 * (ar - 1) + oT);
+                frag_ld_lo(fa, pT + eTA + 16 * ar * PT + 16 * (ar - 1));
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     Frag<OpT> fb;
@@ -571,7 +617,7 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
                 }
             }
             Frag<OpT> ft;
-            frag_ld_lo(ft, sTA + 16 * ar * PT + 16 * ar + oT);
+            frag_ld_lo(ft, pT + eTA + 16 * ar * PT + 16 * ar);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 Frag<OpT> fw;
@@ -597,14 +643,14 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     Frag<OpT> fq;
-                    frag_ld(fq, sLq + 16 * ar * PK + 32 * kb + oK);
+                    frag_ld(fq, pK + 16 * ar * PK + 32 * kb);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) O[ct] = mma(fq, fs[kb][ct], O[ct]);
                 }
 #pragma unroll
                 for (int kb = 0; kb <= ar / 2; ++kb) {
                     Frag<OpT> fb;
-                    frag_ld(fb, sB + 16 * ar * PT + 32 * kb + oT);
+                    frag_ld(fb, pT + eB + 16 * ar * PT + 32 * kb);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) O[ct] = mma(fb, fU[kb][ct], O[ct]);
                 }
@@ -613,7 +659,7 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sO[j * PW + ct * 16 + oOw] = from_f32<TIn>(O[ct][j]);
+                    for (int j = 0; j < 4; ++j) pOw[j * PW + ct * 16] = from_f32<TIn>(O[ct][j]);
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -622,9 +668,9 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
                     const int e = lane + 64 * m;
                     if (NOT % 64 == 0 || e < NOT) {
                         const int row = e / VPRW;
-                        const u32x4_t x = *reinterpret_cast<const KDA_LDS u32x4_t*>(sO + oOr + m * (64 / VPRW) * PW);
+                        const u32x4_t x = *reinterpret_cast<const KDA_LDS u32x4_t*>(pOr + m * (64 / VPRW) * PW);
                         if (c0 + 16 * ar + row < t_end)
-                            *reinterpret_cast<u32x4_t*>(go + (c0 + 16 * ar + m * (64 / VPRW)) * HD + oGo) = x;
+                            *reinterpret_cast<u32x4_t*>(at_byte(go + (c0 + 16 * ar + m * (64 / VPRW)) * HD, pinned_u(boGo))) = x;
                     }
                 }
             }
@@ -633,7 +679,7 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
         // S <- Diag(2^{g_C}) S + K'^T U
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const f32x4_t gam = *reinterpret_cast<const KDA_LDS f32x4_t*>(sE + NT * DK + 16 * it + 4 * lg);
+            const f32x4_t gam = *reinterpret_cast<const KDA_LDS f32x4_t*>(pG + NT * DK + 16 * it);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -641,7 +687,7 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(const PrefillArgs a
 #pragma unroll
             for (int kb = 0; kb < NTB; ++kb) {
                 Frag<OpT> fkp;
-                frag_ld(fkp, sKpT + 16 * it * PT + 32 * kb + oT);
+                frag_ld(fkp, pT + 16 * it * PT + 32 * kb);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) st[it][ct] = mma(fkp, fU[kb][ct], st[it][ct]);
             }
@@ -668,7 +714,7 @@ hipError_t launch_prefill_cfg(const PrefillArgs& a, hipStream_t stream) {
     const long long nblk = groups * 8 * a.n_vs;
     if (nblk <= 0) return hipSuccess;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kda_prefill_kernel<Cfg>, dim3((unsigned)nblk), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(kda_prefill_kernel<Cfg>, dim3((unsigned)nblk), dim3(Cfg::NTH), 0, stream, a);
     return hipGetLastError();
 }
 
