@@ -112,6 +112,7 @@ template <typename T> struct Quad;
 template <> struct Quad<__bf16> {
     typedef u32x2_t raw;
     __device__ __forceinline__ static raw load(const __bf16* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+    __device__ __forceinline__ static raw zero() { return u32x2_t{0u, 0u}; }
     __device__ __forceinline__ static raw load(const KDA_LDS __bf16* p) { return *reinterpret_cast<const KDA_LDS u32x2_t*>(p); }
     __device__ __forceinline__ static float get(raw r, int i) {
         const uint32_t w = i < 2 ? r[0] : r[1];
@@ -126,6 +127,7 @@ template <> struct Quad<__bf16> {
 template <> struct Quad<float> {
     typedef f32x4_t raw;
     __device__ __forceinline__ static raw load(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
+    __device__ __forceinline__ static raw zero() { return f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}; }
     __device__ __forceinline__ static raw load(const KDA_LDS float* p) { return *reinterpret_cast<const KDA_LDS f32x4_t*>(p); }
     __device__ __forceinline__ static float get(raw r, int i) { return r[i]; }
     __device__ __forceinline__ static void store(KDA_LDS float* p, float a, float b, float c, float d) {
@@ -325,6 +327,14 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 pq[i] = QI::load(gq + off);
                 pk[i] = QI::load(gk + off);
             }
+            // rows past the end act as zero queries and keys; this path runs at most once per
+            // unit, so the wait these selects imply costs nothing
+#pragma unroll
+            for (int i = 0; i < TPS; ++i)
+                if (c0 + sg * TPS + i >= t_end) {
+                    pq[i] = QI::zero();
+                    pk[i] = QI::zero();
+                }
             pbeta = gbeta[clampt(c0 + (tid % C)) * a.H];
 #pragma unroll
             for (int m = 0; m < NVV; ++m)
@@ -445,13 +455,13 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                     const float loc = gp[i / G][u] + g[i][u];   // g - rho_a, in [-115.4, 0]
                     const float x = fast_exp2(loc);              // <= 1
                     const float y = fast_exp2(-loc);             // >= 1, at most 2^115.4 = e^80
-                    const float qv = okt[i] ? QI::get(pq[i], u) : 0.0f;
-                    const float kv = okt[i] ? QI::get(pk[i], u) : 0.0f;
+                    const float qv = QI::get(pq[i], u);
+                    const float kv = QI::get(pk[i], u);
                     lq[u] = qv * x;
                     lk[u] = kv * x;
                     kd[u] = kv * y;
                     // K' = k 2^{g_C - g}: the factor above 1 meets only a factor that cannot underflow
-                    kp[u][i] = kv * ((y * fd[u]) * fc[u]);
+                    kp[u][i] = (kd[u] * fd[u]) * fc[u];
                 }
                 QO::store(pA + i * PK, lq[0], lq[1], lq[2], lq[3]);
                 QO::store(pA + eLk + i * PK, lk[0], lk[1], lk[2], lk[3]);
