@@ -73,10 +73,15 @@ kda_status_t check_prefill_shape(int B, int T, int H, int dk, int dv, int chunk,
 
 // The automatic plan: column slices first (no extra work beyond the shared
 // per-chunk tiles), then segments when even that leaves most compute units idle.
-void auto_plan(int B, int T, int H, int dv, int chunk, int* seg_len, int* n_vs) {
+void auto_plan(int B, int T, int H, int dk, int dv, int chunk, bool f32, int* seg_len, int* n_vs) {
     const long long cus = cu_count();
     const long long bh = (long long)B * H;
-    int vs = (dv == 128 && 2 * bh <= cus) ? 2 : 1;
+    // Two column slices only pay where a 128-column workgroup has 4 waves (32 columns each):
+    // halving the columns then halves the state products of every chunk.  With 8 waves a slice
+    // already holds 16 columns per wave, and a second slice would only repeat the decay and
+    // intra-chunk work; the sequence split below is what shortens the chain of chunks.
+    const bool eight = kda::prefill_waves(dk, dv, f32) == 8;
+    int vs = (dv == 128 && !eight && 2 * bh <= cus) ? 2 : 1;
     long long seg = T;
     const long long units = bh * vs;
     if (units > 0 && 2 * units <= cus && (long long)T >= 2 * kMinSegTokens) {
@@ -95,7 +100,7 @@ void auto_plan(int B, int T, int H, int dv, int chunk, int* seg_len, int* n_vs) 
 kda_status_t resolve_plan(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt,
                           int seg_len_in, int n_vs_in, long long* seg_len, int* n_seg, int* n_vs) {
     int a_seg = 0, a_vs = 0;
-    auto_plan(B, T, H, dv, chunk, &a_seg, &a_vs);
+    auto_plan(B, T, H, dk, dv, chunk, dt == KDA_F32, &a_seg, &a_vs);
     long long sl = seg_len_in > 0 ? seg_len_in : a_seg;
     if (seg_len_in < 0 || (seg_len_in > 0 && seg_len_in % chunk != 0)) return KDA_ERR_INVALID_ARGUMENT;
     int vs = n_vs_in > 0 ? n_vs_in : a_vs;
@@ -133,8 +138,8 @@ bool prefill_supported(int dk, int dvw, int chunk, bool f32) {
 
 // Waves per workgroup for a 128-column slice in bf16: 4 (32 columns per wave) or 8 (16 columns
 // per wave, two waves per SIMD).  KDA_PREFILL_WAVES overrides the default (tuning only).
-static int prefill_waves(int dvw, bool f32) {
-    if (f32 || dvw != 128) return 4;
+int prefill_waves(int dk, int dvw, bool f32) {
+    if (f32 || dk != 128 || dvw != 128) return 4;
     static int cached = 0;
     if (cached == 0) {
         const char* e = getenv("KDA_PREFILL_WAVES");
@@ -145,7 +150,7 @@ static int prefill_waves(int dvw, bool f32) {
 
 hipError_t launch_prefill(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a, hipStream_t s) {
     if (!prefill_supported(dk, dvw, chunk, f32)) return hipErrorInvalidValue;
-    const int nw = prefill_waves(dvw, f32);
+    const int nw = prefill_waves(dk, dvw, f32);
     return f32 ? launch_prefill_f32(dk, dvw, nw, chunk, a, s) : launch_prefill_bf16(dk, dvw, nw, chunk, a, s);
 }
 

@@ -58,6 +58,8 @@ struct DecodeArgs {
 
 // dvw = state columns per workgroup (d_v / column slices).
 bool prefill_supported(int dk, int dvw, int chunk, bool f32);
+// Waves per workgroup that launch_prefill uses for a slice of dvw state columns.
+int prefill_waves(int dk, int dvw, bool f32);
 hipError_t launch_prefill(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a,
                           hipStream_t stream);
 hipError_t launch_scan(int dk, const ScanArgs& a, hipStream_t stream);

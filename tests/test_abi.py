@@ -175,10 +175,14 @@ def test_plan_rules(lib):
     assert lib.kda_chunk_prefill_plan(4, 32768, 56, 128, 128, 64, BF16, ctypes.byref(seg),
                                       ctypes.byref(nvs)) == OK
     assert (seg.value, nvs.value) == (32768, 1)
-    # few heads, long sequence: column slices and segments
+    # few heads, long sequence (bf16, 8-wave workgroups): segments, one column slice
     assert lib.kda_chunk_prefill_plan(1, 1 << 20, 16, 128, 128, 64, BF16, ctypes.byref(seg),
                                       ctypes.byref(nvs)) == OK
-    assert nvs.value == 2 and seg.value % 64 == 0 and seg.value < (1 << 20)
+    assert nvs.value == 1 and seg.value % 64 == 0 and seg.value < (1 << 20)
+    # the same in fp32 (4-wave workgroups): column slices and segments
+    assert lib.kda_chunk_prefill_plan(1, 1 << 20, 16, 128, 128, 32, F32, ctypes.byref(seg),
+                                      ctypes.byref(nvs)) == OK
+    assert nvs.value == 2 and seg.value % 32 == 0 and seg.value < (1 << 20)
     # short sequence: never split below the minimum segment length
     assert lib.kda_chunk_prefill_plan(1, 6000, 1, 128, 128, 64, BF16, ctypes.byref(seg),
                                       ctypes.byref(nvs)) == OK
