@@ -13,6 +13,7 @@
 namespace kda {
 hipError_t launch_prefill_bf16(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16_dual(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
 }  // namespace kda
 
 namespace {
@@ -152,6 +153,15 @@ hipError_t launch_prefill(int dk, int dvw, int chunk, bool f32, const PrefillArg
     if (!prefill_supported(dk, dvw, chunk, f32)) return hipErrorInvalidValue;
     const int nw = prefill_waves(dk, dvw, f32);
     return f32 ? launch_prefill_f32(dk, dvw, nw, chunk, a, s) : launch_prefill_bf16(dk, dvw, nw, chunk, a, s);
+}
+
+bool prefill_dual_supported(int dk, int dvw, int chunk, bool f32) {
+    return prefill_supported(dk, dvw, chunk, f32) && !f32 && prefill_waves(dk, dvw, f32) == 8;
+}
+
+hipError_t launch_prefill_dual(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a, hipStream_t s) {
+    if (!prefill_dual_supported(dk, dvw, chunk, f32)) return hipErrorInvalidValue;
+    return launch_prefill_bf16_dual(dk, dvw, prefill_waves(dk, dvw, f32), chunk, a, s);
 }
 
 }  // namespace kda
@@ -303,13 +313,23 @@ kda_status_t kda_chunk_prefill_ex(const void* q, const void* k, const void* v, c
     pm.seg0 = 0;
     pm.n_seg_launch = ns - 1;
     pm.n_units = (int)(bh * (ns - 1));
-    if (kda::launch_prefill(dk, dvw, chunk, f32, pm, s) != hipSuccess) return KDA_ERR_DEVICE;
-
-    PrefillArgs ph = pm;  // H_s: zero start, real values, no output
-    ph.init_mode = 0;
-    ph.zero_values = 0;
-    ph.s_out = wsH;
-    if (kda::launch_prefill(dk, dvw, chunk, f32, ph, s) != hipSuccess) return KDA_ERR_DEVICE;
+    if (kda::prefill_dual_supported(dk, dvw, chunk, f32)) {
+        PrefillArgs pd = pm;  // M_s and H_s together: the decay and intra-chunk work is shared
+        pd.init_mode = 0;
+        pd.zero_values = 0;
+        pd.s_out = wsH;
+        pd.s_aux = wsM;
+        pd.saux_bh_stride = pm.sout_bh_stride;
+        pd.saux_seg_stride = pm.sout_seg_stride;
+        if (kda::launch_prefill_dual(dk, dvw, chunk, f32, pd, s) != hipSuccess) return KDA_ERR_DEVICE;
+    } else {
+        if (kda::launch_prefill(dk, dvw, chunk, f32, pm, s) != hipSuccess) return KDA_ERR_DEVICE;
+        PrefillArgs ph = pm;  // H_s: zero start, real values, no output
+        ph.init_mode = 0;
+        ph.zero_values = 0;
+        ph.s_out = wsH;
+        if (kda::launch_prefill(dk, dvw, chunk, f32, ph, s) != hipSuccess) return KDA_ERR_DEVICE;
+    }
 
     kda::ScanArgs sa;
     sa.M = wsM;

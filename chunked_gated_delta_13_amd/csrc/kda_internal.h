@@ -34,6 +34,12 @@ struct PrefillArgs {
     int n_vs;                 // state-column slices per unit
     int n_units;              // B * H * n_seg_launch
     int zero_values;          // 1: treat v as zeros (transition pass)
+
+    // dual pass (launch_prefill_dual): s_out receives each unit's increment (zero start, real
+    // values) and s_aux its transition (identity columns, zero values); no output rows
+    float* s_aux;
+    long long saux_bh_stride;
+    long long saux_seg_stride;
 };
 
 struct ScanArgs {
@@ -62,6 +68,10 @@ bool prefill_supported(int dk, int dvw, int chunk, bool f32);
 int prefill_waves(int dk, int dvw, bool f32);
 hipError_t launch_prefill(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a,
                           hipStream_t stream);
+// Transition and increment of every unit in one pass (shapes with 8-wave workgroups only).
+bool prefill_dual_supported(int dk, int dvw, int chunk, bool f32);
+hipError_t launch_prefill_dual(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a,
+                               hipStream_t stream);
 hipError_t launch_scan(int dk, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_decode(int dk, bool f32, const DecodeArgs& a, hipStream_t stream);
 // dst[i] = src ? src[i] : 0 for n floats

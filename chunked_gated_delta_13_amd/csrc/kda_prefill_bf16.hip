@@ -28,4 +28,14 @@ hipError_t launch_prefill_bf16(int dk, int dvw, int nw, int chunk, const Prefill
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_prefill_bf16_dual(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s) {
+    using T = __bf16;
+    if (dk == 128 && dvw == 128 && nw == 8) {
+        if (chunk == 64) return launch_prefill_cfg<PrefillCfg<128, 1, 64, T, 8>, true>(a, s);
+        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<128, 1, 32, T, 8>, true>(a, s);
+        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<128, 1, 16, T, 8>, true>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace kda

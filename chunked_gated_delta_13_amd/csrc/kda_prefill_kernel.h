@@ -135,7 +135,10 @@ template <> struct Quad<float> {
     }
 };
 
-template <class Cfg>
+// DUAL: one pass yields both the transition of each unit (identity columns, zero values, kept in
+// `sm`) and its increment (zero start, real values, kept in `st`); the decay and intra-chunk work
+// is shared and no output rows are formed.
+template <class Cfg, bool DUAL>
 __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs a) {
     using TIn = typename Cfg::TIn;
     using OpT = typename Cfg::OpT;
@@ -187,7 +190,8 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     const int col0 = vs * DVW;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in a scalar register
 
     const long long HD = (long long)a.H * DK;  // token stride of every [B, T, H, d] tensor
     const long long base_tok = (long long)b * a.T * HD + (long long)h * DK;
@@ -197,12 +201,26 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     const TIn* gv = reinterpret_cast<const TIn*>(a.v) + base_tok + col0;
     TIn* go = a.o ? reinterpret_cast<TIn*>(a.o) + base_tok + col0 : nullptr;
     const float* gbeta = a.beta + (long long)b * a.T * a.H + h;
-    const bool has_o = go != nullptr;
+    const bool has_o = !DUAL && go != nullptr;
     const bool zero_v = a.zero_values != 0;
 
-    // ---- initial state: lane holds S[16*it + 4*lg + j][colw(ct)] ----
-    f32x4_t st[NIT][NCT];
-    if (a.init_mode == 1) {
+    // ---- initial state: lane holds S[16*it + 4*lg + j][colw(ct)]; in the dual pass column tiles
+    //      NCT..2*NCT-1 hold the transition of the same columns ----
+    constexpr int NCD = DUAL ? 2 * NCT : NCT;
+    f32x4_t st[NIT][NCD];
+    if constexpr (DUAL) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int col = col0 + wave * 16 * NCT + ct * 16 + lr;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    st[it][ct][j] = 0.0f;
+                    st[it][NCT + ct][j] = (16 * it + 4 * lg + j == col) ? 1.0f : 0.0f;
+                }
+            }
+    } else if (a.init_mode == 1) {
         const float* sin = a.s_in + (long long)bh * a.sin_bh_stride + (long long)s * a.sin_seg_stride;
 #pragma unroll
         for (int it = 0; it < NIT; ++it)
@@ -310,7 +328,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
         if (c0 + C <= t_end) {
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
-                pq[i] = QI::load(at_byte(gq + (c0 + i) * HD, pinned_u(boQK)));
+                if constexpr (!DUAL) pq[i] = QI::load(at_byte(gq + (c0 + i) * HD, pinned_u(boQK)));
                 pk[i] = QI::load(at_byte(gk + (c0 + i) * HD, pinned_u(boQK)));
             }
             pbeta = *at_byte(gbeta + c0 * a.H, pinned_u(boB));
@@ -324,7 +342,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
                 const long long off = clampt(c0 + sg * TPS + i) * HD + ch0;
-                pq[i] = QI::load(gq + off);
+                if constexpr (!DUAL) pq[i] = QI::load(gq + off);
                 pk[i] = QI::load(gk + off);
             }
             // rows past the end act as zero queries and keys; this path runs at most once per
@@ -332,7 +350,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
 #pragma unroll
             for (int i = 0; i < TPS; ++i)
                 if (c0 + sg * TPS + i >= t_end) {
-                    pq[i] = QI::zero();
+                    if constexpr (!DUAL) pq[i] = QI::zero();
                     pk[i] = QI::zero();
                 }
             pbeta = gbeta[clampt(c0 + (tid % C)) * a.H];
@@ -455,15 +473,14 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                     const float loc = gp[i / G][u] + g[i][u];   // g - rho_a, in [-115.4, 0]
                     const float x = fast_exp2(loc);              // <= 1
                     const float y = fast_exp2(-loc);             // >= 1, at most 2^115.4 = e^80
-                    const float qv = QI::get(pq[i], u);
                     const float kv = QI::get(pk[i], u);
-                    lq[u] = qv * x;
+                    if constexpr (!DUAL) lq[u] = QI::get(pq[i], u) * x;
                     lk[u] = kv * x;
                     kd[u] = kv * y;
                     // K' = k 2^{g_C - g}: the factor above 1 meets only a factor that cannot underflow
                     kp[u][i] = (kd[u] * fd[u]) * fc[u];
                 }
-                QO::store(pA + i * PK, lq[0], lq[1], lq[2], lq[3]);
+                if constexpr (!DUAL) QO::store(pA + i * PK, lq[0], lq[1], lq[2], lq[3]);
                 QO::store(pA + eLk + i * PK, lk[0], lk[1], lk[2], lk[3]);
                 QO::store(pA + eKd + i * PK, kd[0], kd[1], kd[2], kd[3]);
             }
@@ -487,7 +504,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 for (int kb = 0; kb < NKB; ++kb) {
                     Frag<OpT> fk, fq, fr;
                     frag_ld(fk, pK + eLk + 16 * ar * PK + 32 * kb);
-                    frag_ld(fq, pK + 16 * ar * PK + 32 * kb);
+                    if constexpr (!DUAL) frag_ld(fq, pK + 16 * ar * PK + 32 * kb);
                     frag_ld(fr, pK + eKd + 16 * ac * PK + 32 * kb);
                     if constexpr (ac < ar) {
                         // R = Kd 2^{rho_ar - rho_ac}: multiply by 2^{rho_{m+1} - rho_m} one tile at a
@@ -506,7 +523,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                         for (int j = 0; j < 8; ++j) fr.set(j, val[j]);
                     }
                     accA = mma(fk, fr, accA);
-                    accB = mma(fq, fr, accB);
+                    if constexpr (!DUAL) accB = mma(fq, fr, accB);
                 }
                 const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pG + fBeta + 16 * ar);
                 if constexpr (ac == ar) {
@@ -515,14 +532,14 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                     for (int j = 0; j < 4; ++j) {
                         const int rl = 4 * lg + j;
                         ad[j] = (lr < rl) ? accA[j] * bt4[j] : 0.0f;
-                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
+                        if constexpr (!DUAL) pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
                     }
                     *reinterpret_cast<KDA_LDS f32x4_t*>(pAd + ar * PDB) = ad;  // transposed
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         pW[16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(-accA[j] * bt4[j]);
-                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(accB[j]);
+                        if constexpr (!DUAL) pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(accB[j]);
                     }
                 }
             });
@@ -554,7 +571,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
         } else {
             // K~ = Lk 2^{rho_a}, Q~ = Lq 2^{rho_a} (factors <= 1), in place
 #pragma unroll
-            for (int arr = 0; arr < 2; ++arr) {
+            for (int arr = 0; arr < (DUAL ? 1 : 2); ++arr) {
                 KDA_LDS OpT* base = arr ? pCv : pCv + eLk;
 #pragma unroll
                 for (int m = 0; m < (C + CV_ROWS - 1) / CV_ROWS; ++m) {
@@ -571,56 +588,56 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
         barrier_lds();
 
         // ================= D: state-dependent products =================
-        Frag<OpT> fs[NKB][NCT];   // S as B operand
+        Frag<OpT> fs[NKB][NCD];   // S as B operand
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) acc_pair_frag(fs[kb][ct], st[2 * kb][ct], st[2 * kb + 1][ct], true);
+            for (int ct = 0; ct < NCD; ++ct) acc_pair_frag(fs[kb][ct], st[2 * kb][ct], st[2 * kb + 1][ct], true);
 
         // X = K~ S, then RHS = beta (V - X)
-        f32x4_t Rh[NT][NCT];
+        f32x4_t Rh[NT][NCD];
 #pragma unroll
         for (int ar = 0; ar < NT; ++ar) {
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = zero4();
+            for (int ct = 0; ct < NCD; ++ct) Rh[ar][ct] = zero4();
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 Frag<OpT> fk;
                 frag_ld(fk, pK + eLk + 16 * ar * PK + 32 * kb);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = mma(fk, fs[kb][ct], Rh[ar][ct]);
+                for (int ct = 0; ct < NCD; ++ct) Rh[ar][ct] = mma(fk, fs[kb][ct], Rh[ar][ct]);
             }
             const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pG + fBeta + 16 * ar);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
+            for (int ct = 0; ct < NCD; ++ct) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float vv = zero_v ? 0.0f : to_f32<TIn>(pV[(16 * ar + j) * PV + ct * 16]);
+                    const float vv = (zero_v || ct >= NCT) ? 0.0f : to_f32<TIn>(pV[(16 * ar + j) * PV + ct * 16]);
                     Rh[ar][ct][j] = bt4[j] * (vv - Rh[ar][ct][j]);
                 }
             }
         }
 
         // U by blocked forward substitution: U_a = T_aa (RHS_a - sum_{b<a} A_ab U_b)
-        f32x4_t U[NT][NCT];
-        Frag<OpT> fU[NTB][NCT];
+        f32x4_t U[NT][NCD];
+        Frag<OpT> fU[NTB][NCD];
 #pragma unroll
         for (int ar = 0; ar < NT; ++ar) {
-            f32x4_t W[NCT];
+            f32x4_t W[NCD];
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) W[ct] = Rh[ar][ct];
+            for (int ct = 0; ct < NCD; ++ct) W[ct] = Rh[ar][ct];
 #pragma unroll
             for (int kb = 0; kb < ar / 2; ++kb) {
                 Frag<OpT> fa;
                 frag_ld(fa, pT + eTA + 16 * ar * PT + 32 * kb);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) W[ct] = mma(fa, fU[kb][ct], W[ct]);
+                for (int ct = 0; ct < NCD; ++ct) W[ct] = mma(fa, fU[kb][ct], W[ct]);
             }
             if (ar & 1) {
                 Frag<OpT> fa;
                 frag_ld_lo(fa, pT + eTA + 16 * ar * PT + 16 * (ar - 1));
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
+                for (int ct = 0; ct < NCD; ++ct) {
                     Frag<OpT> fb;
                     acc_pair_frag(fb, U[ar - 1][ct], U[ar - 1][ct], false);
                     W[ct] = mma(fa, fb, W[ct]);
@@ -629,17 +646,17 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
             Frag<OpT> ft;
             frag_ld_lo(ft, pT + eTA + 16 * ar * PT + 16 * ar);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
+            for (int ct = 0; ct < NCD; ++ct) {
                 Frag<OpT> fw;
                 acc_pair_frag(fw, W[ct], W[ct], false);
                 U[ar][ct] = mma(ft, fw, zero4());
             }
             if (ar & 1) {
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) acc_pair_frag(fU[ar / 2][ct], U[ar - 1][ct], U[ar][ct], true);
+                for (int ct = 0; ct < NCD; ++ct) acc_pair_frag(fU[ar / 2][ct], U[ar - 1][ct], U[ar][ct], true);
             } else if (ar == NT - 1) {
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) acc_pair_frag(fU[ar / 2][ct], U[ar][ct], U[ar][ct], false);
+                for (int ct = 0; ct < NCD; ++ct) acc_pair_frag(fU[ar / 2][ct], U[ar][ct], U[ar][ct], false);
             }
         }
 
@@ -691,7 +708,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
         for (int it = 0; it < NIT; ++it) {
             const f32x4_t gam = *reinterpret_cast<const KDA_LDS f32x4_t*>(pG + NT * DK + 16 * it);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+            for (int ct = 0; ct < NCD; ++ct)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) st[it][ct][j] *= gam[j];
 #pragma unroll
@@ -699,12 +716,23 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 Frag<OpT> fkp;
                 frag_ld(fkp, pT + 16 * it * PT + 32 * kb);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) st[it][ct] = mma(fkp, fU[kb][ct], st[it][ct]);
+                for (int ct = 0; ct < NCD; ++ct) st[it][ct] = mma(fkp, fU[kb][ct], st[it][ct]);
             }
         }
     }
 
     // ---- final state ----
+    if constexpr (DUAL) {
+        float* sx = a.s_aux + (long long)bh * a.saux_bh_stride + (long long)s * a.saux_seg_stride;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int col = col0 + wave * 16 * NCT + ct * 16 + lr;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sx[(long long)(16 * it + 4 * lg + j) * DK + col] = st[it][NCT + ct][j];
+            }
+    }
     if (a.s_out && (a.out_seg < 0 || a.out_seg == s)) {
         float* so = a.s_out + (long long)bh * a.sout_bh_stride + (long long)s * a.sout_seg_stride;
 #pragma unroll
@@ -718,13 +746,13 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     }
 }
 
-template <class Cfg>
+template <class Cfg, bool DUAL = false>
 hipError_t launch_prefill_cfg(const PrefillArgs& a, hipStream_t stream) {
     const long long groups = ((long long)a.n_units + 7) / 8;
     const long long nblk = groups * 8 * a.n_vs;
     if (nblk <= 0) return hipSuccess;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kda_prefill_kernel<Cfg>, dim3((unsigned)nblk), dim3(Cfg::NTH), 0, stream, a);
+    hipLaunchKernelGGL((kda_prefill_kernel<Cfg, DUAL>), dim3((unsigned)nblk), dim3(Cfg::NTH), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -178,6 +178,18 @@ def test_prefill_column_split_matches_unsplit():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+def test_prefill_split_one_pass_matches_two_pass():
+    """With one column slice the transitions and increments come from one shared pass; with two
+    slices from two separate passes.  Columns are independent, so both give the same bits."""
+    inp = _case(1, 900, 2, 128, "bf16", decay="slow", s0=1.0, seed=29)
+    o1, s1 = _run_prefill(inp, 64, seg_len=192, n_vs=1)
+    o2, s2 = _run_prefill(inp, 64, seg_len=192, n_vs=2)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    o_ref, s_ref = _oracle(inp)
+    assert_close("o", o1, o_ref, "bf16")
+    assert_close("S_T", s1, s_ref, "bf16")
+
+
 def test_prefill_in_place_state():
     inp = _case(2, 150, 2, 128, "bf16", s0=1.0, seed=26)
     o_ref, s_ref = _oracle(inp)
