@@ -107,6 +107,15 @@ constexpr int pair_row(int pi) {
     return ar;
 }
 
+// Wave that forms the pi-th tile pair.  With 8 waves and 4 row tiles the two pairs beyond the
+// eighth go to waves that hold a diagonal (cheaper) pair; wave 0 keeps one pair because it also
+// inverts the diagonal blocks.
+constexpr int pair_owner(int pi, int nw) {
+    if (nw == 8 && pi == 8) return 5;
+    if (nw == 8 && pi == 9) return 2;
+    return pi % nw;
+}
+
 // Four adjacent elements (a channel quad) of an input or operand array.
 template <typename T> struct Quad;
 template <> struct Quad<__bf16> {
@@ -451,14 +460,25 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 fd[u] = fast_exp2(nx[u] - rho[u]);   // 2^{rho_{a+1} - rho_a} in [2^-115.4, 1]
                 fc[u] = fast_exp2(gC[u] - nx[u]);    // 2^{g_C - rho_{a+1}} in (0, 1]
             }
-            if (sg == 0) {
+            // tables 2^{rho_a} (a <= NT) and 2^{rho_{a+1} - rho_a}: row a is formed by the segment
+            // sg = a * TSTEP, so the exponentials are spread over several waves
+            {
+                constexpr int TSTEP = NSEG / (NT + 1) > 0 ? NSEG / (NT + 1) : 1;
+                static_assert(NSEG >= NT + 1, "one segment per table row");
+                if (sg % TSTEP == 0 && sg / TSTEP <= NT) {
+                    const int t2 = sg / TSTEP;
+                    f32x4_t r0 = Rt[0], r1 = Rt[NT >= 1 ? 1 : 0];
 #pragma unroll
-                for (int t2 = 0; t2 <= NT; ++t2) {
+                    for (int a2 = 1; a2 <= NT; ++a2)
+                        if (t2 == a2) {
+                            r0 = Rt[a2];
+                            r1 = Rt[a2 < NT ? a2 + 1 : a2];
+                        }
                     f32x4_t e4, d4;
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        e4[u] = fast_exp2(Rt[t2][u]);
-                        d4[u] = t2 < NT ? fast_exp2(Rt[t2 + 1][u] - Rt[t2][u]) : 0.0f;
+                        e4[u] = fast_exp2(r0[u]);
+                        d4[u] = fast_exp2(r1[u] - r0[u]);
                     }
                     *reinterpret_cast<KDA_LDS f32x4_t*>(pCh + t2 * DK) = e4;
                     if (t2 < NT) *reinterpret_cast<KDA_LDS f32x4_t*>(pCh + fD + t2 * DK) = d4;
@@ -498,7 +518,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 constexpr int pi = decltype(PIc)::value;
                 constexpr int ar = pair_row(pi);
                 constexpr int ac = pi - ar * (ar + 1) / 2;
-                if (pi % NW != wave) return;   // wave-uniform
+                if (pair_owner(pi, NW) != wave) return;   // wave-uniform
                 f32x4_t accA = zero4(), accB = zero4();
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
@@ -554,17 +574,22 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 float col[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) col[r] = (r == jj) ? 1.0f : 0.0f;
+                // column i of A_aa (only the quads below the diagonal), fetched two steps ahead
+                f32x4_t acol[15][4];
+                auto fetch = [&](auto I) {
+                    constexpr int i = decltype(I)::value;
 #pragma unroll
-                for (int i = 0; i < 15; ++i) {
-                    float acol[16];
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        if (4 * q4 + 3 > i) acol[i][q4] = *reinterpret_cast<const KDA_LDS f32x4_t*>(pAdT + i * PD + 4 * q4);
+                };
+                fetch(std::integral_constant<int, 0>{});
+                fetch(std::integral_constant<int, 1>{});
+                static_for<0, 15>([&](auto I) {
+                    constexpr int i = decltype(I)::value;
+                    if constexpr (i + 2 < 15) fetch(std::integral_constant<int, i + 2>{});
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x4_t v4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pAdT + i * PD + 4 * q4);
-                        acol[4 * q4] = v4[0]; acol[4 * q4 + 1] = v4[1]; acol[4 * q4 + 2] = v4[2]; acol[4 * q4 + 3] = v4[3];
-                    }
-#pragma unroll
-                    for (int r = i + 1; r < 16; ++r) col[r] -= acol[r] * col[i];
-                }
+                    for (int r = i + 1; r < 16; ++r) col[r] -= acol[i][r / 4][r % 4] * col[i];
+                });
 #pragma unroll
                 for (int r = 0; r < 16; ++r) pE1[r * PT] = from_f32<OpT>(col[r]);
             }
