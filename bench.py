@@ -160,6 +160,65 @@ def bench_decode(kda, gen, steps=1000, pool=8):
     return w, wall, ev
 
 
+def spec_bytes(N, H, d, m, accepted):
+    """Algorithmic HBM bytes of one verify (state read, drafted inputs, outputs) and one commit.
+    A commit moves only the sequences that accept at least one token: their state is read and
+    written, and their accepted tokens' k, v, log_alpha and beta are read (queries not needed)."""
+    state_head = d * d * 4
+    verify = N * H * state_head + N * m * H * (3 * d * 2 + d * 4 + 4 + d * 2)
+    moved = int((accepted > 0).sum())
+    toks = int(accepted.clamp(0, m).sum())
+    commit = moved * H * 2 * state_head + toks * H * (2 * d * 2 + d * 4 + 4)
+    return verify, commit
+
+
+def bench_spec(kda, gen, steps=200, pool=8):
+    import torch
+    w = gen.SPEC_WORKLOADS["spec_n256_m4"]
+    log(f"[spec] {w.note}: state {w.N*w.H*w.dk*w.dv*4/1e9:.3f} GB, {pool} distinct drafted blocks")
+    S = gen.make_state(w.N, w.H, w.dk, w.dv, w.s0_std, seed=w.seed, device="cuda")
+    blocks = [gen.make_spec_inputs(w.N, w.m, w.H, w.dk, w.dv, w.dtype, w.decay,
+                                   seed=w.seed * 10**6 + i, device="cuda") for i in range(pool)]
+    o = torch.empty((w.N, w.m, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    it = [0]
+
+    def verify():
+        b = blocks[it[0] % pool]
+        it[0] += 1
+        kda.spec_verify(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], S, o=o)
+
+    def commit():
+        b = blocks[it[0] % pool]
+        it[0] += 1
+        kda.spec_commit(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], S, b["accepted"])
+
+    def both():
+        b = blocks[it[0] % pool]
+        it[0] += 1
+        kda.spec_verify(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], S, o=o)
+        kda.spec_commit(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], S, b["accepted"])
+
+    _, ev_v = time_loop(verify, steps, 5, stream)
+    _, ev_c = time_loop(commit, steps, 5, stream)
+    wall, ev_b = time_loop(both, steps, 5, stream)
+    assert torch.isfinite(S).all()
+    acc_mean = sum(float(b["accepted"].float().mean()) for b in blocks) / pool
+    per = [spec_bytes(w.N, w.H, w.dk, w.m, b["accepted"].cpu()) for b in blocks]
+    vb = sum(p[0] for p in per) / pool
+    cb = sum(p[1] for p in per) / pool
+    res = {"workload": w.note, "steps": steps, "m": w.m,
+           "verify_us": ev_v / steps * 1e6, "verify_GBps": vb / (ev_v / steps) / 1e9,
+           "commit_us": ev_c / steps * 1e6, "commit_GBps": cb / (ev_c / steps) / 1e9,
+           "step_us": ev_b / steps * 1e6,
+           "frac_of_hbm_peak": (vb + cb) / (ev_b / steps) / 1e9 / HBM_PEAK_GBS,
+           "accepted_tokens_per_s": w.N * acc_mean * steps / wall,
+           "alg_bytes_per_step": vb + cb}
+    log(f"[spec] verify {res['verify_us']:.1f} us ({res['verify_GBps']:.0f} GB/s), commit "
+        f"{res['commit_us']:.1f} us ({res['commit_GBps']:.0f} GB/s)")
+    return res
+
+
 def cpu_baseline(gen_inputs, w, budget_s=15.0):
     """Oracle (float64, OpenMP) on the host cores over a bounded sample of the prefill workload:
     the first P (sequence, head) pairs in sequence-major order, all T tokens each."""
@@ -210,6 +269,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-spec", action="store_true")
+    ap.add_argument("--spec-only", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -238,6 +299,9 @@ def main():
         torch.cuda.synchronize()
         log("[calibration] 3 copies of 1 GiB (1073741824 bytes read + written each)")
         del src, dst
+    if args.spec_only:
+        log(json.dumps(bench_spec(kda, gen)))
+        return
     if args.decode_only:
         wd, dwall, dev_s = bench_decode(kda, gen, args.decode_steps)
         step_s = dev_s / args.decode_steps
@@ -294,6 +358,8 @@ def main():
                             "traffic": profiled_traffic("kda_decode_kernel_n256.md",
                                                         ["kda_decode.hip", "kda_device.h"]),
                             "tokens_per_s": wd.N * args.decode_steps / dwall}
+    if not args.prefill_only and not args.no_spec:
+        result["spec_decode"] = bench_spec(kda, gen)
     if not args.prefill_only and not args.no_long:
         wl, lwall, lev = bench_long(kda, gen, max(2, args.steps // 5), 1)
         nsteps = max(2, args.steps // 5)

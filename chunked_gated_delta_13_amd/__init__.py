@@ -148,3 +148,54 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None):
                              _ptr(o), N, H, dk, dv, code, ctypes.c_void_p(stream))
     _lib.check(st, "kda_decode_step")
     return o
+
+
+def _spec_inputs(q, k, v, log_alpha, beta, S, where):
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [N, m, H, dk]")
+    N, m, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(where + " runs on a HIP device; got a tensor on " + str(dev))
+    _check_tensor("q", q, q.dtype, (N, m, H, dk), dev)
+    _check_tensor("k", k, q.dtype, (N, m, H, dk), dev)
+    _check_tensor("v", v, q.dtype, (N, m, H, dv), dev)
+    _check_tensor("log_alpha", log_alpha, torch.float32, (N, m, H, dk), dev)
+    _check_tensor("beta", beta, torch.float32, (N, m, H), dev)
+    _check_tensor("S", S, torch.float32, (N, H, dk, dv), dev)
+    return N, m, H, dk, dv, dev
+
+
+def spec_verify(q, k, v, log_alpha, beta, S, *, o=None):
+    """Outputs of m drafted tokens per sequence ([N, m, H, ...] inputs) from state S.
+
+    S is not modified.  Returns o [N, m, H, dv]."""
+    torch = _torch()
+    lib = _lib.load()
+    N, m, H, dk, dv, dev = _spec_inputs(q, k, v, log_alpha, beta, S, "spec_verify")
+    if o is None:
+        o = torch.empty((N, m, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _check_tensor("o", o, q.dtype, (N, m, H, dv), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.kda_spec_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                             _ptr(o), N, m, H, dk, dv, _dtype_code(q.dtype),
+                             ctypes.c_void_p(stream))
+    _lib.check(st, "kda_spec_verify")
+    return o
+
+
+def spec_commit(q, k, v, log_alpha, beta, S, accepted):
+    """Advance S in place over the first accepted[n] of the m cached drafted tokens of each
+    sequence (the inputs given to spec_verify).  ``accepted`` is an int32 device tensor [N]."""
+    torch = _torch()
+    lib = _lib.load()
+    N, m, H, dk, dv, dev = _spec_inputs(q, k, v, log_alpha, beta, S, "spec_commit")
+    _check_tensor("accepted", accepted, torch.int32, (N,), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.kda_spec_commit(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                             _ptr(accepted), N, m, H, dk, dv, _dtype_code(q.dtype),
+                             ctypes.c_void_p(stream))
+    _lib.check(st, "kda_spec_commit")

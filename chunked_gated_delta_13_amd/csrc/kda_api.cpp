@@ -69,7 +69,55 @@ kda_status_t check_prefill_shape(int B, int T, int H, int dk, int dv, int chunk,
     if (!kda::prefill_supported(dk, dv, chunk, dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
     long long n = 0;
     if (!mul_ok((long long)B * T, (long long)H * dk, &n)) return KDA_ERR_INVALID_ARGUMENT;
+    // lane offsets inside one chunk are 32-bit byte offsets: 64 token rows of H * dk fp32 values
+    if ((long long)H * dk > (1LL << 22)) return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * H > (1LL << 27)) return KDA_ERR_UNSUPPORTED;   // units fit the launch grid
     return KDA_OK;
+}
+
+// Drafted blocks up to this many tokens run as a token loop on the decode kernel (state read
+// once, tokens in order on chip); longer blocks run as a chunked prefill.
+constexpr int kSpecTokenLoopMax = kda::kDecodeMaxTokens;
+
+// Shape, pointer, alignment and overlap checks of a speculative block (token-loop path).
+// o (verify) or accepted (commit) is the one of the two that is not NULL.
+kda_status_t check_spec_pointers(const void* q, const void* k, const void* v, const float* log_alpha,
+                                 const float* beta, const float* S, const void* o, const int* accepted, int N,
+                                 int m, int H, int dk, int dv, kda_dtype_t dt) {
+    if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_INVALID_ARGUMENT;
+    if (dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+    long long ntok_ll = 0, nh = 0;
+    if (!mul_ok((long long)N * m, H, &ntok_ll) || !mul_ok(N, H, &nh)) return KDA_ERR_INVALID_ARGUMENT;
+    if (nh * (dk / 64) > 0x7fffffffLL) return KDA_ERR_UNSUPPORTED;
+    if (N == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !log_alpha || !beta || !S || (!o && !accepted)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(log_alpha, 16) || !aligned(S, 16) ||
+        !aligned(beta, 4) || (o && !aligned(o, 16)) || (accepted && !aligned(accepted, 4)))
+        return KDA_ERR_INVALID_ARGUMENT;
+    const size_t esz = dt == KDA_BF16 ? 2 : 4;
+    const size_t ntok = (size_t)ntok_ll;
+    const Range rs = range_of(S, (size_t)nh * dk * dv * sizeof(float));
+    const Range ins[] = {range_of(q, ntok * dk * esz), range_of(k, ntok * dk * esz), range_of(v, ntok * dv * esz),
+                         range_of(log_alpha, ntok * dk * sizeof(float)), range_of(beta, ntok * sizeof(float))};
+    if (o) {   // verify: o must not overlap any input or the state
+        const Range ro = range_of(o, ntok * dv * esz);
+        for (const Range& r : ins)
+            if (overlap(ro, r)) return KDA_ERR_INVALID_ARGUMENT;
+        if (overlap(ro, rs)) return KDA_ERR_INVALID_ARGUMENT;
+    } else {   // commit: the state is written and must not overlap any input
+        for (const Range& r : ins)
+            if (overlap(rs, r)) return KDA_ERR_INVALID_ARGUMENT;
+        if (overlap(rs, range_of(accepted, (size_t)N * sizeof(int)))) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    return KDA_OK;
+}
+
+// Chunk length for an m-token speculative block: the smallest supported chunk that holds it.
+int spec_chunk(int m, kda_dtype_t dt) {
+    if (m <= 16) return 16;
+    if (m <= 32 || dt == KDA_F32) return 32;
+    return 64;
 }
 
 // The automatic plan: column slices first (no extra work beyond the shared
@@ -366,6 +414,117 @@ kda_status_t kda_chunk_prefill(const void* q, const void* k, const void* v, cons
                                 workspace, workspace_bytes, stream);
 }
 
+kda_status_t kda_spec_verify(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const float* S, void* o, int N, int m, int H, int dk, int dv,
+                             kda_dtype_t dt, void* stream) {
+    if (N < 0 || H < 0 || m < 1) return KDA_ERR_INVALID_ARGUMENT;
+    if (N > 0 && H > 0 && !S) return KDA_ERR_INVALID_ARGUMENT;
+    if (m > kSpecTokenLoopMax) {
+        // a long block runs from S as one short chunked prefill; no state is written
+        return kda_chunk_prefill_ex(q, k, v, log_alpha, beta, S, o, nullptr, N, m, H, dk, dv, spec_chunk(m, dt),
+                                    dt, 0, 0, nullptr, 0, stream);
+    }
+    const kda_status_t st = check_spec_pointers(q, k, v, log_alpha, beta, S, o, nullptr, N, m, H, dk, dv, dt);
+    if (st != KDA_OK || N == 0 || H == 0) return st;
+    (void)hipGetLastError();
+    kda::DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.beta = beta;
+    a.S = const_cast<float*>(S);   // read only: write_state is 0
+    a.o = o;
+    a.NH = (long long)N * H;
+    a.H = H;
+    a.m = m;
+    a.lens = nullptr;
+    a.write_state = 0;
+    if (kda::launch_decode(dk, dt == KDA_F32, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
+kda_status_t kda_spec_commit(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, float* S, const int* accepted, int N, int m, int H, int dk,
+                             int dv, kda_dtype_t dt, void* stream) {
+    if (N < 0 || H < 0 || m < 1) return KDA_ERR_INVALID_ARGUMENT;
+    if (m <= kSpecTokenLoopMax) {
+        const kda_status_t st0 =
+            check_spec_pointers(q, k, v, log_alpha, beta, S, nullptr, accepted, N, m, H, dk, dv, dt);
+        if (st0 != KDA_OK || N == 0 || H == 0) return st0;
+        (void)hipGetLastError();
+        kda::DecodeArgs d;
+        memset(&d, 0, sizeof(d));
+        d.q = q;
+        d.k = k;
+        d.v = v;
+        d.log_alpha = log_alpha;
+        d.beta = beta;
+        d.S = S;
+        d.o = nullptr;
+        d.NH = (long long)N * H;
+        d.H = H;
+        d.m = m;
+        d.lens = accepted;
+        d.write_state = 1;
+        if (kda::launch_decode(dk, dt == KDA_F32, d, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+            return KDA_ERR_DEVICE;
+        return KDA_OK;
+    }
+    const int chunk = spec_chunk(m, dt);
+    kda_status_t st = check_prefill_shape(N, m, H, dk, dv, chunk, dt);
+    if (st != KDA_OK) return st;
+    long long sl = 0;
+    int ns = 0, vs = 0;
+    st = resolve_plan(N, m, H, dk, dv, chunk, dt, 0, 0, &sl, &ns, &vs);
+    if (st != KDA_OK) return st;
+    if (ns != 1) return KDA_ERR_UNSUPPORTED;
+    if (N == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !log_alpha || !beta || !S || !accepted) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(log_alpha, 16) || !aligned(S, 16) ||
+        !aligned(beta, 4) || !aligned(accepted, 4))
+        return KDA_ERR_INVALID_ARGUMENT;
+    const size_t esz = dt == KDA_BF16 ? 2 : 4;
+    const size_t ntok = (size_t)N * m * H;
+    const Range rs = range_of(S, (size_t)N * H * dk * dv * sizeof(float));
+    const Range ins[] = {range_of(q, ntok * dk * esz), range_of(k, ntok * dk * esz), range_of(v, ntok * dv * esz),
+                         range_of(log_alpha, ntok * dk * sizeof(float)), range_of(beta, ntok * sizeof(float)),
+                         range_of(accepted, (size_t)N * sizeof(int))};
+    for (const Range& r : ins)
+        if (overlap(rs, r)) return KDA_ERR_INVALID_ARGUMENT;
+
+    (void)hipGetLastError();
+    const long long SS = (long long)dk * dv;
+    PrefillArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.beta = beta;
+    a.o = nullptr;            // the outputs were produced by the verify call
+    a.s_in = S;               // each workgroup reads its own columns of S before it writes them
+    a.sin_bh_stride = SS;
+    a.init_mode = 1;
+    a.s_out = S;
+    a.sout_bh_stride = SS;
+    a.out_seg = -1;
+    a.T = m;
+    a.B = N;
+    a.H = H;
+    a.seg_len = m;
+    a.n_seg_launch = 1;
+    a.n_vs = vs;
+    a.n_units = N * H;
+    a.lens = accepted;
+    if (kda::launch_prefill(dk, dv / vs, chunk, dt == KDA_F32, a, reinterpret_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return KDA_ERR_DEVICE;
+    return KDA_OK;
+}
+
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
                              const float* beta, float* S, void* o, int N, int H, int dk, int dv,
                              kda_dtype_t dt, void* stream) {
@@ -398,6 +557,10 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const 
     a.S = S;
     a.o = o;
     a.NH = nh;
+    a.H = H;
+    a.m = 1;
+    a.lens = nullptr;
+    a.write_state = 1;
     (void)hipGetLastError();
     if (kda::launch_decode(dk, dt == KDA_F32, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_ERR_DEVICE;

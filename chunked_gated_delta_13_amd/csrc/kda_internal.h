@@ -40,6 +40,10 @@ struct PrefillArgs {
     float* s_aux;
     long long saux_bh_stride;
     long long saux_seg_stride;
+
+    // per-sequence token counts (device, [B]; clamped to [0, T]) or nullptr: sequence b then
+    // stops after lens[b] tokens, and its final state is the state after those tokens
+    const int* lens;
 };
 
 struct ScanArgs {
@@ -51,15 +55,22 @@ struct ScanArgs {
     int n_seg;
 };
 
+// Decode step (m = 1) or a block of m <= kDecodeMaxTokens tokens per (sequence, head) run from
+// the state on chip.
+constexpr int kDecodeMaxTokens = 16;
 struct DecodeArgs {
-    const void* q;            // [NH, DK]
+    const void* q;            // [N, m, H, DK]
     const void* k;
-    const void* v;            // [NH, DK]
-    const float* log_alpha;   // [NH, DK]
-    const float* beta;        // [NH]
-    float* S;                 // [NH, DK, DK]
-    void* o;                  // [NH, DK]
-    long long NH;
+    const void* v;            // [N, m, H, DK]
+    const float* log_alpha;   // [N, m, H, DK]
+    const float* beta;        // [N, m, H]
+    float* S;                 // [N, H, DK, DK]
+    void* o;                  // [N, m, H, DK] or nullptr (no outputs)
+    long long NH;             // N * H
+    int H;
+    int m;                    // tokens per block
+    const int* lens;          // per-sequence token counts (device, clamped to [0, m]) or nullptr
+    int write_state;          // 1: write the state after the block back to S
 };
 
 // dvw = state columns per workgroup (d_v / column slices).

@@ -195,7 +195,12 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     const int b = bh / a.H;
     const int s = a.seg0 + sl;
     const long long t_begin = (long long)s * a.seg_len;
-    const long long t_end = (t_begin + a.seg_len < a.T) ? t_begin + a.seg_len : a.T;
+    long long t_end = (t_begin + a.seg_len < a.T) ? t_begin + a.seg_len : a.T;
+    if (a.lens) {   // ragged: this sequence stops after lens[b] tokens
+        const long long l = a.lens[b];
+        const long long lc = l < 0 ? 0 : (l > a.T ? a.T : l);
+        if (t_end > lc) t_end = lc;
+    }
     const int col0 = vs * DVW;
 
     const int tid = threadIdx.x;
@@ -594,19 +599,28 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 for (int r = 0; r < 16; ++r) pE1[r * PT] = from_f32<OpT>(col[r]);
             }
         } else {
-            // K~ = Lk 2^{rho_a}, Q~ = Lq 2^{rho_a} (factors <= 1), in place
+            // K~ = Lk 2^{rho_a}, Q~ = Lq 2^{rho_a} (factors <= 1), in place; all loads issued first
+            constexpr int NARR = DUAL ? 1 : 2;
+            constexpr int NM = (C + CV_ROWS - 1) / CV_ROWS;
+            typename QO::raw x[NARR][NM];
+            f32x4_t e4[NM];
 #pragma unroll
-            for (int arr = 0; arr < (DUAL ? 1 : 2); ++arr) {
-                KDA_LDS OpT* base = arr ? pCv : pCv + eLk;
+            for (int m = 0; m < NM; ++m) {
+                if (cvRow0 + m * CV_ROWS < C) {
+                    e4[m] = *reinterpret_cast<const KDA_LDS f32x4_t*>(pCe + ((cvRow0 + m * CV_ROWS) >> 4) * DK);
 #pragma unroll
-                for (int m = 0; m < (C + CV_ROWS - 1) / CV_ROWS; ++m) {
-                    const int row = cvRow0 + m * CV_ROWS;
-                    if (row >= C) break;
-                    KDA_LDS OpT* p = base + m * CV_ROWS * PK;
-                    const typename QO::raw x = QO::load(p);
-                    const f32x4_t e4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pCe + (row >> 4) * DK);
-                    QO::store(p, QO::get(x, 0) * e4[0], QO::get(x, 1) * e4[1], QO::get(x, 2) * e4[2],
-                              QO::get(x, 3) * e4[3]);
+                    for (int arr = 0; arr < NARR; ++arr)
+                        x[arr][m] = QO::load((arr ? pCv : pCv + eLk) + m * CV_ROWS * PK);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                if (cvRow0 + m * CV_ROWS < C) {
+#pragma unroll
+                    for (int arr = 0; arr < NARR; ++arr)
+                        QO::store((arr ? pCv : pCv + eLk) + m * CV_ROWS * PK, QO::get(x[arr][m], 0) * e4[m][0],
+                                  QO::get(x[arr][m], 1) * e4[m][1], QO::get(x[arr][m], 2) * e4[m][2],
+                                  QO::get(x[arr][m], 3) * e4[m][3]);
                 }
             }
         }

@@ -85,6 +85,30 @@ DECODE_WORKLOADS = {
                                   steps=1000, note="256 sequences x 56 heads, 1000 steps"),
 }
 
+@dataclass(frozen=True)
+class SpecWorkload:
+    """Speculative decoding: m drafted tokens per sequence, verified then partly committed."""
+    name: str
+    N: int
+    m: int
+    H: int
+    dk: int
+    dv: int
+    dtype: str
+    decay: str
+    s0_std: float
+    seed: int
+    note: str = ""
+
+
+# Decode-shaped batch (256 sequences x 56 heads) with 4 drafted tokens per step; the accepted
+# count of each sequence is uniform on {0, ..., m}.  The pages give no draft length; 4 is a
+# common setting for one drafted block.
+SPEC_WORKLOADS = {
+    "spec_n256_m4": SpecWorkload("spec_n256_m4", 256, 4, 56, 128, 128, "bf16", "sig2", 0.02, 7,
+                                 note="256 sequences x 56 heads, 4 drafted tokens per step"),
+}
+
 _TORCH_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
@@ -155,3 +179,14 @@ def make_state(N, H, dk, dv, s0_std=0.02, seed=0, device="cpu"):
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed))
     return (s0_std * _normal((N, H, dk, dv), gen, device)).contiguous()
+
+
+def make_spec_inputs(N, m, H, dk, dv, dtype="bf16", decay="sig2", seed=0, device="cpu"):
+    """One drafted block: q, k [N, m, H, dk], v [N, m, H, dv], log_alpha, beta [N, m, H], and
+    accepted [N] (int32, uniform on {0, ..., m}), drawn after the token inputs."""
+    d = make_prefill_inputs(N, m, H, dk, dv, dtype, decay, 0.0, seed, 0.0, device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) + 7919)
+    acc = torch.randint(0, m + 1, (N,), generator=gen, device=device, dtype=torch.int64)
+    return {"q": d["q"], "k": d["k"], "v": d["v"], "log_alpha": d["log_alpha"], "beta": d["beta"],
+            "accepted": acc.to(torch.int32).contiguous()}

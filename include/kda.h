@@ -150,6 +150,45 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              const float *log_alpha, const float *beta, float *S, void *o,
                              int N, int H, int dk, int dv, kda_dtype_t dtype, void *stream);
 
+/*
+ * Speculative decoding, verify step: m >= 1 drafted tokens per sequence, run from the current
+ * state S, with the outputs of all m tokens written to o and S left unchanged.  Pages: "Kimi
+ * K3's architecture" (orkas.ai), "The bill comes due in the serving stack" (the state is
+ * updated in place, so a rejected draft cannot be undone; the projected inputs are kept and
+ * the state is rebuilt on chip).  Blocks of up to 16 tokens run as a token loop with the state
+ * held on chip (read once); longer blocks run as one short chunked prefill (chunk 32 or 64).
+ *
+ *   q, k       [N, m, H, dk]  dtype          drafted queries, keys
+ *   v          [N, m, H, dv]  dtype
+ *   log_alpha  [N, m, H, dk]  fp32           (clamped to [-5, 0])
+ *   beta       [N, m, H]      fp32
+ *   S          [N, H, dk, dv] fp32           state before the block (read only)
+ *   o          [N, m, H, dv]  dtype  (out)   o[n, t] = S_t^T q_t for t < m
+ *   dk == dv   64 or 128
+ * N == 0 or H == 0 is a no-op.  Errors as for kda_chunk_prefill.
+ */
+kda_status_t kda_spec_verify(const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta, const float *S,
+                             void *o, int N, int m, int H, int dk, int dv, kda_dtype_t dtype,
+                             void *stream);
+
+/*
+ * Speculative decoding, commit step: advance S in place over the first accepted[n] of the m
+ * cached drafted tokens of sequence n (the same inputs given to kda_spec_verify), rebuilding
+ * the state from those inputs instead of rolling it back.  Same source as kda_spec_verify.
+ *
+ *   q, k, v, log_alpha, beta   as for kda_spec_verify
+ *   S          [N, H, dk, dv] fp32  in/out   state before the block on entry, state after the
+ *                                            accepted tokens on return
+ *   accepted   [N]            int32 DEVICE   tokens to keep per sequence; values outside
+ *                                            [0, m] are clamped on the device (0 leaves S as is)
+ * No output rows are written.  S must not overlap any input.  N == 0 or H == 0 is a no-op.
+ */
+kda_status_t kda_spec_commit(const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta, float *S,
+                             const int *accepted, int N, int m, int H, int dk, int dv,
+                             kda_dtype_t dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

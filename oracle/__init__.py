@@ -115,3 +115,35 @@ def decode_step(q, k, v, log_alpha, beta, S, nthreads: int | None = None):
     o, st = prefill(q[:, None], k[:, None], v[:, None], la[:, None], bt[:, None], s,
                     nthreads=nthreads)
     return o[:, 0], st
+
+
+def spec_verify(q, k, v, log_alpha, beta, S, nthreads: int | None = None):
+    """Speculative decoding, verify step: the outputs of m drafted tokens per sequence, run
+    from the state S, with S itself left as it was.
+
+    Source: "Kimi K3's architecture" (orkas.ai), section "The bill comes due in the serving
+    stack": the state is updated in place, so a rejected draft cannot be undone; the projected
+    inputs are kept and the state is rebuilt from them.  Verifying is therefore the recurrence
+    over the m drafted tokens from S, with its final state discarded.
+
+    q, k, log_alpha: [N, m, H, dk]; v: [N, m, H, dv]; beta: [N, m, H]; S: [N, H, dk, dv].
+    Returns o [N, m, H, dv] (float64).
+    """
+    o, _ = prefill(q, k, v, log_alpha, beta, S, nthreads=nthreads)
+    return o
+
+
+def spec_commit(q, k, v, log_alpha, beta, S, accepted, nthreads: int | None = None):
+    """Speculative decoding, commit step: the state after the first accepted[n] drafted tokens
+    of sequence n, rebuilt from the kept inputs (same source as spec_verify).  Counts outside
+    [0, m] are clamped.  Returns S_new [N, H, dk, dv] (float64); S is not modified."""
+    q, k, v, la, bt, s = (_f64(x) for x in (q, k, v, log_alpha, beta, S))
+    acc = np.asarray(accepted.detach().cpu() if hasattr(accepted, "detach") else accepted)
+    N, m = q.shape[:2]
+    out = np.empty_like(s)
+    for n in range(N):
+        a = int(min(max(int(acc[n]), 0), m))
+        _, st = prefill(q[n:n + 1, :a], k[n:n + 1, :a], v[n:n + 1, :a], la[n:n + 1, :a],
+                        bt[n:n + 1, :a], s[n:n + 1], nthreads=nthreads)
+        out[n] = st[0]
+    return out

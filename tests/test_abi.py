@@ -204,3 +204,27 @@ def test_binding_refuses_host_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load(str(tmp_path / "libkda.so"))
+
+
+def _spec(lib, fn, N=2, m=4, H=3, dk=128, dv=128, dt=BF16, q=_ptrs(0), k=_ptrs(1), v=_ptrs(2),
+          la=_ptrs(3), beta=_ptrs(4), S=_ptrs(5), last=_ptrs(6)):
+    vp = ctypes.c_void_p
+    f = getattr(lib, fn)
+    return f(vp(q), vp(k), vp(v), vp(la), vp(beta), vp(S), vp(last), N, m, H, dk, dv, dt, None)
+
+
+@pytest.mark.parametrize("fn", ["kda_spec_verify", "kda_spec_commit"])
+def test_spec_validation(lib, host_only, fn):
+    assert _spec(lib, fn, m=0) == INVALID
+    assert _spec(lib, fn, N=-1) == INVALID
+    assert _spec(lib, fn, dk=96, dv=96) == UNSUPPORTED
+    assert _spec(lib, fn, dt=4) == INVALID
+    assert _spec(lib, fn, S=None) == INVALID
+    assert _spec(lib, fn, last=None) == INVALID          # o for verify, accepted for commit
+    assert _spec(lib, fn, q=_ptrs(0) + 8) == INVALID     # misaligned
+    assert _spec(lib, fn, N=0, q=None, k=None, v=None, la=None, beta=None, S=None, last=None) == OK
+
+
+def test_spec_commit_state_must_not_overlap_inputs(lib, host_only):
+    assert _spec(lib, "kda_spec_commit", S=_ptrs(2) + 64) == INVALID
+    assert _spec(lib, "kda_spec_commit", last=_ptrs(5) + 16) == INVALID   # accepted inside S

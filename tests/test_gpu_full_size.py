@@ -111,3 +111,34 @@ def test_decode_1000_steps_sampled_states():
     torch.cuda.synchronize()
     assert_close("S after 1000 steps", S[ns, hs][None], S_ref, "bf16")
     assert torch.isfinite(S).all()
+
+
+def test_spec_decode_full_batch_sampled_states():
+    """The speculative-decoding workload at its full size (256 sequences x 56 heads, 4 drafted
+    tokens, seeded accepted counts), 50 verify + commit rounds, checked on 48 sampled
+    (sequence, head) states and their outputs against the oracle."""
+    kda = _kda()
+    w = gen.SPEC_WORKLOADS["spec_n256_m4"]
+    print(f"spec: {w.note}", flush=True)
+    S = gen.make_state(w.N, w.H, w.dk, w.dv, w.s0_std, seed=w.seed, device="cuda")
+    rng = np.random.default_rng(1)
+    picks = [(int(n), int(h)) for n, h in zip(rng.integers(0, w.N, 48), rng.integers(0, w.H, 48))]
+    ns = torch.tensor([p[0] for p in picks])
+    hs = torch.tensor([p[1] for p in picks])
+    S_ref = to_f64(S[ns, hs])[:, None]                   # [P, 1, dk, dv]: one head per sequence
+    o = torch.empty((w.N, w.m, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    for rnd in range(50):
+        b = gen.make_spec_inputs(w.N, w.m, w.H, w.dk, w.dv, w.dtype, w.decay,
+                                 seed=w.seed * 10**6 + rnd, device="cuda")
+        kda.spec_verify(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], S, o=o)
+        kda.spec_commit(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], S, b["accepted"])
+        sub = {k: b[k][ns, :, hs][:, :, None].cpu() for k in ("q", "k", "v", "log_alpha", "beta")}
+        acc = b["accepted"][ns].cpu().numpy()
+        o_ref = oracle.spec_verify(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"], S_ref)
+        S_ref = oracle.spec_commit(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"], S_ref, acc)
+        if rnd % 10 == 9:
+            torch.cuda.synchronize()
+            assert_close(f"o round {rnd}", o[ns, :, hs], o_ref[:, :, 0], "bf16")
+    torch.cuda.synchronize()
+    assert_close("S after 50 rounds", S[ns, hs], S_ref[:, 0], "bf16")
+    assert torch.isfinite(S).all()
