@@ -115,6 +115,29 @@ def bench_prefill(kda, gen, steps, warmup):
     return w, d, wall, ev, plan
 
 
+def bench_prefill_ckpt(kda, w, d, steps, warmup, every=4096):
+    """Model-width prefill that also checkpoints the state every `every` tokens (a sparse subset
+    of the 512-token hash endpoints: every eighth one)."""
+    import torch
+    o = torch.empty_like(d["v"])
+    st = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    ck = torch.empty((w.B, w.T // every, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.chunk_prefill_ckpt(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
+                               chunk=w.chunk, ckpt_every=every, o=o, S_T=st, S_ckpt=ck)
+
+    wall, ev = time_loop(step, steps, warmup, stream)
+    ck_bytes = ck.numel() * 4
+    alg = prefill_bytes(w.B, w.T, w.H, w.dk) + ck_bytes
+    log(f"[ckpt] {steps} steps: events {ev*1e3:.2f} ms")
+    return {"every": every, "checkpoints_per_sequence": w.T // every, "ms_per_step": ev / steps * 1e3,
+            "checkpoint_bytes": ck_bytes, "alg_bytes_per_launch": alg,
+            "achieved_GBps": alg / (ev / steps) / 1e9,
+            "frac_of_hbm_peak": alg / (ev / steps) / 1e9 / HBM_PEAK_GBS}
+
+
 def bench_long(kda, gen, steps, warmup):
     import torch
     w = gen.WORKLOADS["long_1m"]
@@ -270,6 +293,7 @@ def main():
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-spec", action="store_true")
+    ap.add_argument("--no-ckpt", action="store_true")
     ap.add_argument("--spec-only", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
@@ -342,6 +366,10 @@ def main():
                      "useful_tflops": useful_tflops,
                      "useful_frac_of_bf16_peak": useful_tflops / BF16_PEAK_TFLOPS},
     }
+    if not args.prefill_only and not args.no_ckpt:
+        ckr = bench_prefill_ckpt(kda, w, d, args.steps, args.warmup)
+        ckr["overhead_vs_plain"] = ckr["ms_per_step"] / (launch_s * 1e3) - 1.0
+        result["prefill_checkpoints"] = ckr
     if not args.prefill_only and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, w)
     del d

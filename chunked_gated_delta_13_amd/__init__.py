@@ -83,6 +83,25 @@ def chunk_prefill(q, k, v, log_alpha, beta, S0=None, chunk=64, *, seg_len=0, n_v
     ``S_T`` may be passed as ``S0`` itself to update the state in place.
     ``seg_len`` / ``n_vs`` force a sequence-split plan (0 = the library's choice).
     """
+    o, S_T, _ = _prefill(q, k, v, log_alpha, beta, S0, chunk, seg_len, n_vs, o, S_T,
+                         return_state, workspace, 0, None)
+    return o, S_T
+
+
+def chunk_prefill_ckpt(q, k, v, log_alpha, beta, S0=None, chunk=64, *, ckpt_every, seg_len=0,
+                       n_vs=0, o=None, S_T=None, S_ckpt=None, return_state=True, workspace=None):
+    """chunk_prefill that also returns state checkpoints for prefix reuse.
+
+    Returns (o, S_T, S_ckpt) with S_ckpt [B, T // ckpt_every, H, dk, dv]: the state after the
+    first (i + 1) * ckpt_every tokens of each sequence.  ``ckpt_every`` is a positive multiple
+    of ``chunk``.
+    """
+    return _prefill(q, k, v, log_alpha, beta, S0, chunk, seg_len, n_vs, o, S_T, return_state,
+                    workspace, ckpt_every, S_ckpt)
+
+
+def _prefill(q, k, v, log_alpha, beta, S0, chunk, seg_len, n_vs, o, S_T, return_state,
+             workspace, ckpt_every, S_ckpt):
     torch = _torch()
     lib = _lib.load()
     if q.dim() != 4:
@@ -112,13 +131,19 @@ def chunk_prefill(q, k, v, log_alpha, beta, S0=None, chunk=64, *, seg_len=0, n_v
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if ckpt_every:
+        n_ckpt = T // ckpt_every if ckpt_every > 0 else 0
+        if S_ckpt is None:
+            S_ckpt = torch.empty((B, n_ckpt, H, dk, dv), dtype=torch.float32, device=dev)
+        else:
+            _check_tensor("S_ckpt", S_ckpt, torch.float32, (B, n_ckpt, H, dk, dv), dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = lib.kda_chunk_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                  _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, code,
-                                  seg_len, n_vs, _ptr(workspace), ws_bytes,
-                                  ctypes.c_void_p(stream))
+    st = lib.kda_chunk_prefill_ckpt(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                    _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, code,
+                                    int(ckpt_every), _ptr(S_ckpt), seg_len, n_vs,
+                                    _ptr(workspace), ws_bytes, ctypes.c_void_p(stream))
     _lib.check(st, "kda_chunk_prefill")
-    return o, S_T
+    return o, S_T, S_ckpt
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, o=None):

@@ -255,8 +255,19 @@ kda_status_t kda_chunk_prefill_ex(const void* q, const void* k, const void* v, c
                                   const float* beta, const float* S0, void* o, float* S_T, int B, int T,
                                   int H, int dk, int dv, int chunk, kda_dtype_t dt, int seg_len, int n_vs,
                                   void* workspace, size_t workspace_bytes, void* stream) {
+    return kda_chunk_prefill_ckpt(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk, dt, 0, nullptr,
+                                  seg_len, n_vs, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_prefill_ckpt(const void* q, const void* k, const void* v, const float* log_alpha,
+                                    const float* beta, const float* S0, void* o, float* S_T, int B, int T,
+                                    int H, int dk, int dv, int chunk, kda_dtype_t dt, int ckpt_every,
+                                    float* S_ckpt, int seg_len, int n_vs, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
     kda_status_t st = check_prefill_shape(B, T, H, dk, dv, chunk, dt);
     if (st != KDA_OK) return st;
+    if (ckpt_every < 0 || (ckpt_every > 0 && ckpt_every % chunk != 0)) return KDA_ERR_INVALID_ARGUMENT;
+    const int n_ckpt = ckpt_every > 0 ? T / ckpt_every : 0;
     long long sl = 0;
     int ns = 0, vs = 0;
     st = resolve_plan(B, T, H, dk, dv, chunk, dt, seg_len, n_vs, &sl, &ns, &vs);
@@ -288,6 +299,19 @@ kda_status_t kda_chunk_prefill_ex(const void* q, const void* k, const void* v, c
         }
         if (S0 && overlap(ro, range_of(S0, state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
         if (S_T && overlap(ro, range_of(S_T, state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if (n_ckpt > 0 && B > 0 && H > 0) {   // checkpoints: [B, n_ckpt, H, dk, dv], written only
+        if (!S_ckpt || !aligned(S_ckpt, 16)) return KDA_ERR_INVALID_ARGUMENT;
+        const Range rc = range_of(S_ckpt, (size_t)B * n_ckpt * H * dk * dv * sizeof(float));
+        const Range others[] = {range_of(q, ntok * dk * esz), range_of(k, ntok * dk * esz),
+                                range_of(v, ntok * dv * esz), range_of(log_alpha, ntok * dk * sizeof(float)),
+                                range_of(beta, ntok * sizeof(float)), range_of(o, ntok * dv * esz)};
+        for (const Range& r : others)
+            if (overlap(rc, r)) return KDA_ERR_INVALID_ARGUMENT;
+        if (S0 && overlap(rc, range_of(S0, state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
+        if (S_T && overlap(rc, range_of(S_T, state_bytes))) return KDA_ERR_INVALID_ARGUMENT;
+        if (workspace && overlap(rc, range_of(workspace, workspace_for(B, H, dk, dv, ns))))
+            return KDA_ERR_INVALID_ARGUMENT;
     }
     const size_t need = workspace_for(B, H, dk, dv, ns);
     if (need > 0) {
@@ -338,6 +362,11 @@ kda_status_t kda_chunk_prefill_ex(const void* q, const void* k, const void* v, c
         a.n_seg_launch = 1;
         a.n_units = B * H;
         a.zero_values = 0;
+        if (n_ckpt > 0) {
+            a.s_ckpt = S_ckpt;
+            a.ckpt_every = ckpt_every;
+            a.n_ckpt = n_ckpt;
+        }
         if (kda::launch_prefill(dk, dvw, chunk, f32, a, s) != hipSuccess) return KDA_ERR_DEVICE;
         return KDA_OK;
     }
@@ -402,6 +431,11 @@ kda_status_t kda_chunk_prefill_ex(const void* q, const void* k, const void* v, c
     pf.seg0 = 0;
     pf.n_seg_launch = ns;
     pf.n_units = (int)(bh * ns);
+    if (n_ckpt > 0) {   // only the pass that runs from the true entry states writes checkpoints
+        pf.s_ckpt = S_ckpt;
+        pf.ckpt_every = ckpt_every;
+        pf.n_ckpt = n_ckpt;
+    }
     if (kda::launch_prefill(dk, dvw, chunk, f32, pf, s) != hipSuccess) return KDA_ERR_DEVICE;
     return KDA_OK;
 }

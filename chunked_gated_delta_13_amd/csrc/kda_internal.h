@@ -44,6 +44,12 @@ struct PrefillArgs {
     // per-sequence token counts (device, [B]; clamped to [0, T]) or nullptr: sequence b then
     // stops after lens[b] tokens, and its final state is the state after those tokens
     const int* lens;
+
+    // checkpoints [B, n_ckpt, H, DK, DK] or nullptr: the state after every ckpt_every tokens
+    // (a multiple of the chunk), i.e. after tokens ckpt_every * (i + 1), i < n_ckpt
+    float* s_ckpt;
+    int ckpt_every;
+    int n_ckpt;
 };
 
 struct ScanArgs {

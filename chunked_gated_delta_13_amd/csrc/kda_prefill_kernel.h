@@ -758,6 +758,25 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 for (int ct = 0; ct < NCD; ++ct) st[it][ct] = mma(fkp, fU[kb][ct], st[it][ct]);
             }
         }
+
+        // checkpoint: the state after a multiple of ckpt_every tokens (full chunks only)
+        if constexpr (!DUAL) {
+            if (a.s_ckpt) {
+                const long long pend = c0 + C;
+                if (pend <= t_end && pend % a.ckpt_every == 0) {
+                    const long long ci = pend / a.ckpt_every - 1;
+                    float* sc = a.s_ckpt + (((long long)b * a.n_ckpt + ci) * a.H + h) * (long long)(DK * DK);
+#pragma unroll
+                    for (int it = 0; it < NIT; ++it)
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct) {
+                            const int col = col0 + wave * 16 * NCT + ct * 16 + lr;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) sc[(long long)(16 * it + 4 * lg + j) * DK + col] = st[it][ct][j];
+                        }
+                }
+            }
+        }
     }
 
     // ---- final state ----

@@ -131,6 +131,28 @@ kda_status_t kda_chunk_prefill_ex(const void *q, const void *k, const void *v,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_prefill_ex that also checkpoints the state for prefix reuse: S_ckpt[b, i] is the
+ * state after the first (i + 1) * ckpt_every tokens of sequence b, for i < T / ckpt_every.
+ * Pages: "Kimi K3's architecture" (orkas.ai), "The bill comes due in the serving stack" (a
+ * prefix-cache hit needs the recurrent state restorable at the same boundary as the token
+ * pages; the state is checkpointed only at a sparse subset of the 512-token hash endpoints,
+ * e.g. ckpt_every = 4096).
+ *
+ *   ckpt_every  0 (no checkpoints: identical to kda_chunk_prefill_ex) or a positive multiple
+ *               of `chunk`
+ *   S_ckpt      [B, T / ckpt_every, H, dk, dv] fp32, written only; must not overlap any other
+ *               argument (may be NULL when T < ckpt_every)
+ * Other arguments, plans, workspace and errors as for kda_chunk_prefill_ex.
+ */
+kda_status_t kda_chunk_prefill_ckpt(const void *q, const void *k, const void *v,
+                                    const float *log_alpha, const float *beta, const float *S0,
+                                    void *o, float *S_T,
+                                    int B, int T, int H, int dk, int dv, int chunk,
+                                    kda_dtype_t dtype, int ckpt_every, float *S_ckpt,
+                                    int seg_len, int n_vs,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One decode step for N independent sequences: exactly one token of the
  * recurrence, with the state read and written in place.  Pages: "Inside Kimi
  * K3", sequence paragraph (constant cost per new token); "Kimi K3's

@@ -147,3 +147,31 @@ def spec_commit(q, k, v, log_alpha, beta, S, accepted, nthreads: int | None = No
                         bt[n:n + 1, :a], s[n:n + 1], nthreads=nthreads)
         out[n] = st[0]
     return out
+
+
+def prefill_ckpt(q, k, v, log_alpha, beta, S0, ckpt_every, nthreads: int | None = None):
+    """The recurrence with state checkpoints for prefix reuse: returns (o, S_T, S_ckpt) where
+    S_ckpt[b, i] is the state after the first (i + 1) * ckpt_every tokens (i < T // ckpt_every),
+    shaped [B, T // ckpt_every, H, dk, dv].
+
+    Source: "Kimi K3's architecture" (orkas.ai), section "The bill comes due in the serving
+    stack": a prefix-cache hit needs the recurrent state restorable at the same boundary as the
+    cached token pages, so the state is checkpointed at a sparse subset of the 512-token hash
+    endpoints.  The run is taken piece by piece between consecutive checkpoint positions, each
+    piece starting from the state the previous one ended in.
+    """
+    q, k, v, la, bt = (_f64(x) for x in (q, k, v, log_alpha, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    s = np.zeros((B, H, dk, dv)) if S0 is None else _f64(S0)
+    n = T // ckpt_every
+    o = np.empty((B, T, H, dv))
+    ck = np.empty((B, n, H, dk, dv))
+    bounds = [i * ckpt_every for i in range(n + 1)] + ([T] if n * ckpt_every < T else [])
+    for i in range(len(bounds) - 1):
+        a, e = bounds[i], bounds[i + 1]
+        o[:, a:e], s = prefill(q[:, a:e], k[:, a:e], v[:, a:e], la[:, a:e], bt[:, a:e], s,
+                               nthreads=nthreads)
+        if i < n:
+            ck[:, i] = s
+    return o, s, ck

@@ -228,3 +228,20 @@ def test_spec_validation(lib, host_only, fn):
 def test_spec_commit_state_must_not_overlap_inputs(lib, host_only):
     assert _spec(lib, "kda_spec_commit", S=_ptrs(2) + 64) == INVALID
     assert _spec(lib, "kda_spec_commit", last=_ptrs(5) + 16) == INVALID   # accepted inside S
+
+
+def _ckpt(lib, every=128, S_ckpt=_ptrs(8), T=1000, chunk=64, **kw):
+    args = _ok_ptrs()
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return lib.kda_chunk_prefill_ckpt(vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["la"]),
+                                      vp(args["beta"]), None, vp(args["o"]), None, 2, T, 3, 128, 128,
+                                      chunk, BF16, every, vp(S_ckpt), 0, 0, None, 0, None)
+
+
+def test_ckpt_validation(lib, host_only):
+    assert _ckpt(lib, every=100) == INVALID          # not a multiple of the chunk
+    assert _ckpt(lib, every=-64) == INVALID
+    assert _ckpt(lib, S_ckpt=None) == INVALID         # T >= every needs the buffer
+    assert _ckpt(lib, S_ckpt=_ptrs(8) + 4) == INVALID  # misaligned
+    assert _ckpt(lib, S_ckpt=_ptrs(2) + 256) == INVALID   # over v
