@@ -138,6 +138,27 @@ def bench_prefill_ckpt(kda, w, d, steps, warmup, every=4096):
             "frac_of_hbm_peak": alg / (ev / steps) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_prefill_gate(kda, gen, w, d, steps, warmup):
+    """Model-width prefill with the fused bounded gate: bf16 raw gate pre-activations replace the
+    fp32 log-decay (1284 instead of 1540 algorithmic bytes per token-head)."""
+    import torch
+    g = gen.make_gate(w.B, w.T, w.H, w.dk, w.dtype, seed=w.seed, device="cuda")
+    o = torch.empty_like(d["v"])
+    st = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.chunk_prefill_gate(d["q"], d["k"], d["v"], g, d["beta"], d["S0"], chunk=w.chunk, o=o, S_T=st)
+
+    wall, ev = time_loop(step, steps, warmup, stream)
+    del g
+    alg = prefill_bytes(w.B, w.T, w.H, w.dk) - w.B * w.T * w.H * w.dk * 2
+    log(f"[gate] {steps} steps: events {ev*1e3:.2f} ms")
+    return {"ms_per_step": ev / steps * 1e3, "tokens_per_s": w.B * w.T * steps / wall,
+            "alg_bytes_per_launch": alg, "achieved_GBps": alg / (ev / steps) / 1e9,
+            "frac_of_hbm_peak": alg / (ev / steps) / 1e9 / HBM_PEAK_GBS}
+
+
 def bench_long(kda, gen, steps, warmup):
     import torch
     w = gen.WORKLOADS["long_1m"]
@@ -294,6 +315,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-spec", action="store_true")
     ap.add_argument("--no-ckpt", action="store_true")
+    ap.add_argument("--no-gate", action="store_true")
     ap.add_argument("--spec-only", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
@@ -370,6 +392,8 @@ def main():
         ckr = bench_prefill_ckpt(kda, w, d, args.steps, args.warmup)
         ckr["overhead_vs_plain"] = ckr["ms_per_step"] / (launch_s * 1e3) - 1.0
         result["prefill_checkpoints"] = ckr
+    if not args.prefill_only and not args.no_gate:
+        result["prefill_fused_gate"] = bench_prefill_gate(kda, gen, w, d, args.steps, args.warmup)
     if not args.prefill_only and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, w)
     del d

@@ -175,6 +175,47 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None):
     return o
 
 
+def chunk_prefill_gate(q, k, v, gate, beta, S0=None, chunk=64, *, seg_len=0, n_vs=0, o=None,
+                       S_T=None, return_state=True, workspace=None):
+    """chunk_prefill with the bounded gate fused: ``gate`` [B, T, H, dk] (bf16) is the raw gate
+    pre-activation x, and log alpha = -5 * sigmoid(x) is formed in the kernel.  bf16 inputs with
+    dk == dv == 128 only.  Returns (o, S_T)."""
+    torch = _torch()
+    lib = _lib.load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_prefill_gate runs on a HIP device; got a tensor on " + str(dev))
+    code = _dtype_code(q.dtype)
+    for name, t, shape in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+                           ("gate", gate, (B, T, H, dk))):
+        _check_tensor(name, t, q.dtype, shape, dev)
+    _check_tensor("beta", beta, torch.float32, (B, T, H), dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _check_tensor("o", o, q.dtype, (B, T, H, dv), dev)
+    if S_T is None and return_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _check_tensor("S_T", S_T, torch.float32, (B, H, dk, dv), dev)
+    need = int(lib.kda_chunk_prefill_workspace_bytes(B, T, H, dk, dv, chunk, code, seg_len))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.kda_chunk_prefill_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0),
+                                    _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, code, seg_len, n_vs,
+                                    _ptr(workspace), ws_bytes, ctypes.c_void_p(stream))
+    _lib.check(st, "kda_chunk_prefill_gate")
+    return o, S_T
+
+
 def _spec_inputs(q, k, v, log_alpha, beta, S, where):
     torch = _torch()
     if q.dim() != 4:

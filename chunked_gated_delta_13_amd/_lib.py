@@ -38,6 +38,8 @@ SIGNATURES = {
                                   _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "kda_chunk_prefill_ckpt": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _i, _i, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _vp, _sz, _vp]),
+    "kda_chunk_prefill_gate": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "kda_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _i, _i, _i, _i, _i, _vp]),
     "kda_spec_verify": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,

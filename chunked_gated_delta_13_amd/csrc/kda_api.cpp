@@ -14,6 +14,8 @@ namespace kda {
 hipError_t launch_prefill_bf16(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16_dual(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16_gate(int dk, int dvw, int nw, int chunk, bool dual, const PrefillArgs& a,
+                                    hipStream_t s);
 }  // namespace kda
 
 namespace {
@@ -171,6 +173,11 @@ size_t workspace_for(int B, int H, int dk, int dv, int n_seg) {
     return bh * mats * sizeof(float);
 }
 
+kda_status_t prefill_entry(const void* q, const void* k, const void* v, const float* log_alpha, const void* gate,
+                           bool gmode, const float* beta, const float* S0, void* o, float* S_T, int B, int T, int H, int dk,
+                           int dv, int chunk, kda_dtype_t dt, int ckpt_every, float* S_ckpt, int seg_len,
+                           int n_vs, void* workspace, size_t workspace_bytes, void* stream);
+
 }  // namespace
 
 namespace kda {
@@ -200,6 +207,7 @@ int prefill_waves(int dk, int dvw, bool f32) {
 hipError_t launch_prefill(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a, hipStream_t s) {
     if (!prefill_supported(dk, dvw, chunk, f32)) return hipErrorInvalidValue;
     const int nw = prefill_waves(dk, dvw, f32);
+    if (a.gate) return f32 ? hipErrorInvalidValue : launch_prefill_bf16_gate(dk, dvw, nw, chunk, false, a, s);
     return f32 ? launch_prefill_f32(dk, dvw, nw, chunk, a, s) : launch_prefill_bf16(dk, dvw, nw, chunk, a, s);
 }
 
@@ -209,6 +217,7 @@ bool prefill_dual_supported(int dk, int dvw, int chunk, bool f32) {
 
 hipError_t launch_prefill_dual(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a, hipStream_t s) {
     if (!prefill_dual_supported(dk, dvw, chunk, f32)) return hipErrorInvalidValue;
+    if (a.gate) return launch_prefill_bf16_gate(dk, dvw, prefill_waves(dk, dvw, f32), chunk, true, a, s);
     return launch_prefill_bf16_dual(dk, dvw, prefill_waves(dk, dvw, f32), chunk, a, s);
 }
 
@@ -264,8 +273,35 @@ kda_status_t kda_chunk_prefill_ckpt(const void* q, const void* k, const void* v,
                                     int H, int dk, int dv, int chunk, kda_dtype_t dt, int ckpt_every,
                                     float* S_ckpt, int seg_len, int n_vs, void* workspace,
                                     size_t workspace_bytes, void* stream) {
+    return prefill_entry(q, k, v, log_alpha, nullptr, false, beta, S0, o, S_T, B, T, H, dk, dv, chunk, dt, ckpt_every,
+                         S_ckpt, seg_len, n_vs, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_prefill_gate(const void* q, const void* k, const void* v, const void* gate,
+                                    const float* beta, const float* S0, void* o, float* S_T, int B, int T,
+                                    int H, int dk, int dv, int chunk, kda_dtype_t dt, int seg_len, int n_vs,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_entry(q, k, v, nullptr, gate, true, beta, S0, o, S_T, B, T, H, dk, dv, chunk, dt, 0, nullptr,
+                         seg_len, n_vs, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Every prefill entry point: the decay input is log_alpha (fp32) or, with gmode, gate (bf16 raw
+// gate pre-activation).
+kda_status_t prefill_entry(const void* q, const void* k, const void* v, const float* log_alpha, const void* gate,
+                           bool gmode, const float* beta, const float* S0, void* o, float* S_T, int B, int T, int H, int dk,
+                           int dv, int chunk, kda_dtype_t dt, int ckpt_every, float* S_ckpt, int seg_len,
+                           int n_vs, void* workspace, size_t workspace_bytes, void* stream) {
     kda_status_t st = check_prefill_shape(B, T, H, dk, dv, chunk, dt);
     if (st != KDA_OK) return st;
+    if (gmode && (dt != KDA_BF16 || !kda::prefill_dual_supported(dk, dv, chunk, false)))
+        return KDA_ERR_UNSUPPORTED;   // 8-wave bf16 shapes only
+    if (gmode && n_vs > 1) return KDA_ERR_UNSUPPORTED;
+    const void* decay_in = gmode ? gate : static_cast<const void*>(log_alpha);
+    const size_t decay_esz = gmode ? 2 : sizeof(float);
     if (ckpt_every < 0 || (ckpt_every > 0 && ckpt_every % chunk != 0)) return KDA_ERR_INVALID_ARGUMENT;
     const int n_ckpt = ckpt_every > 0 ? T / ckpt_every : 0;
     long long sl = 0;
@@ -285,12 +321,12 @@ kda_status_t kda_chunk_prefill_ckpt(const void* q, const void* k, const void* v,
     if (S0 && S_T && S0 != S_T && overlap(range_of(S0, state_bytes), range_of(S_T, state_bytes)))
         return KDA_ERR_INVALID_ARGUMENT;
     if (T > 0) {
-        if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARGUMENT;
+        if (!q || !k || !v || !decay_in || !beta || !o) return KDA_ERR_INVALID_ARGUMENT;
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-            !aligned(log_alpha, 16) || !aligned(beta, 4))
+            !aligned(decay_in, 16) || !aligned(beta, 4))
             return KDA_ERR_INVALID_ARGUMENT;
         const Range ins[] = {range_of(q, ntok * dk * esz), range_of(k, ntok * dk * esz),
-                             range_of(v, ntok * dv * esz), range_of(log_alpha, ntok * dk * sizeof(float)),
+                             range_of(v, ntok * dv * esz), range_of(decay_in, ntok * dk * decay_esz),
                              range_of(beta, ntok * sizeof(float))};
         const Range ro = range_of(o, ntok * dv * esz);
         for (const Range& r : ins) {
@@ -304,7 +340,7 @@ kda_status_t kda_chunk_prefill_ckpt(const void* q, const void* k, const void* v,
         if (!S_ckpt || !aligned(S_ckpt, 16)) return KDA_ERR_INVALID_ARGUMENT;
         const Range rc = range_of(S_ckpt, (size_t)B * n_ckpt * H * dk * dv * sizeof(float));
         const Range others[] = {range_of(q, ntok * dk * esz), range_of(k, ntok * dk * esz),
-                                range_of(v, ntok * dv * esz), range_of(log_alpha, ntok * dk * sizeof(float)),
+                                range_of(v, ntok * dv * esz), range_of(decay_in, ntok * dk * decay_esz),
                                 range_of(beta, ntok * sizeof(float)), range_of(o, ntok * dv * esz)};
         for (const Range& r : others)
             if (overlap(rc, r)) return KDA_ERR_INVALID_ARGUMENT;
@@ -341,6 +377,7 @@ kda_status_t kda_chunk_prefill_ckpt(const void* q, const void* k, const void* v,
     a.k = k;
     a.v = v;
     a.log_alpha = log_alpha;
+    a.gate = gate;
     a.beta = beta;
     a.T = T;
     a.B = B;
@@ -439,6 +476,10 @@ kda_status_t kda_chunk_prefill_ckpt(const void* q, const void* k, const void* v,
     if (kda::launch_prefill(dk, dvw, chunk, f32, pf, s) != hipSuccess) return KDA_ERR_DEVICE;
     return KDA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 kda_status_t kda_chunk_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
                                const float* beta, const float* S0, void* o, float* S_T, int B, int T, int H,

@@ -10,9 +10,10 @@ struct PrefillArgs {
     const void* q;            // [B, T, H, DK]   bf16 or fp32
     const void* k;            // [B, T, H, DK]
     const void* v;            // [B, T, H, DK]   (d_v == d_k)
-    const float* log_alpha;   // [B, T, H, DK]
+    const float* log_alpha;   // [B, T, H, DK]   (nullptr in the gate mode)
     const float* beta;        // [B, T, H]
     void* o;                  // [B, T, H, DK] or nullptr (no output)
+    const void* gate;         // [B, T, H, DK] bf16 raw gate pre-activation, or nullptr
 
     // initial state of a unit (b, h, s): s_in + bh * sin_bh_stride + s * sin_seg_stride
     const float* s_in;

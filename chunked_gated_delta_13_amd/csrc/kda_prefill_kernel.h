@@ -71,13 +71,12 @@ struct PrefillCfg {
     static constexpr int VPRW = 16 * NCT / VEL;                 // vectors per wave output row
     static constexpr int NOT = 16 * VPRW;                       // vectors per wave output tile
     static constexpr int NOTL = (NOT + 63) / 64;                // per lane
-    static constexpr int NDMA = C * DK * 4 / 1024;              // 1 KiB log-decay loads per chunk
+    static constexpr int NDMA = C * DK * 4 / 1024;              // 1 KiB fp32 log-decay loads per chunk
     static constexpr int NQT = C * DK / 4;                      // quads per [C][DK] array
 
     static_assert(TPS >= 1 && 16 % TPS == 0, "segment must sit inside one tile");
     static_assert(TPS % G == 0, "segment holds whole decay groups");
     static_assert(DK % 32 == 0 && C % 16 == 0 && NT <= 4, "shape");
-    static_assert(NDMA % NW == 0, "log-decay loads split evenly over the waves");
     static_assert(NTH % VPR == 0, "value rows split evenly over the threads");
     static constexpr int CV_ROWS = (NTH - 64) / (DK / 4);       // rows per in-place scaling step
     static_assert((NTH - 64) % (DK / 4) == 0, "in-place scaling covers whole rows");
@@ -147,7 +146,9 @@ template <> struct Quad<float> {
 // DUAL: one pass yields both the transition of each unit (identity columns, zero values, kept in
 // `sm`) and its increment (zero start, real values, kept in `st`); the decay and intra-chunk work
 // is shared and no output rows are formed.
-template <class Cfg, bool DUAL>
+// GATE: the decay input is the raw gate pre-activation x (bf16) and log alpha = -5 sigmoid(x) is
+// formed on load, in place of an fp32 log alpha.
+template <class Cfg, bool DUAL, bool GATE>
 __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs a) {
     using TIn = typename Cfg::TIn;
     using OpT = typename Cfg::OpT;
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     constexpr int DVW = Cfg::DVW, NQ = Cfg::NQ, NSEG = Cfg::NSEG, TPS = Cfg::TPS;
     constexpr int SPT = Cfg::SPT, G = Cfg::G, GPT = Cfg::GPT, PK = Cfg::PK, PT = Cfg::PT, PV = Cfg::PV, PW = Cfg::PW;
     constexpr int PD = Cfg::PD, PDB = Cfg::PDB, VEL = Cfg::VEL, VPR = Cfg::VPR, NV = Cfg::NV, NVV = Cfg::NVV;
-    constexpr int VPRW = Cfg::VPRW, NOT = Cfg::NOT, NOTL = Cfg::NOTL, NDMA = Cfg::NDMA;
+    constexpr int VPRW = Cfg::VPRW, NOT = Cfg::NOT, NOTL = Cfg::NOTL;
     constexpr int NQT = Cfg::NQT, NW = Cfg::NW, NTH = Cfg::NTH, CV_ROWS = Cfg::CV_ROWS;
     constexpr int NIT = DK / 16;   // 16-row tiles of the state
     constexpr int NKB = DK / 32;   // 32-channel contraction blocks
@@ -211,7 +212,10 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     const long long base_tok = (long long)b * a.T * HD + (long long)h * DK;
     const TIn* gq = reinterpret_cast<const TIn*>(a.q) + base_tok;
     const TIn* gk = reinterpret_cast<const TIn*>(a.k) + base_tok;
-    const float* gla = a.log_alpha + base_tok;
+    constexpr int LAE = GATE ? 2 : 4;                          // bytes per decay-input element
+    const char* gla = GATE ? reinterpret_cast<const char*>(a.gate) + base_tok * 2
+                           : reinterpret_cast<const char*>(a.log_alpha + base_tok);
+    const long long HDL = HD * LAE;                            // token stride of the decay input, bytes
     const TIn* gv = reinterpret_cast<const TIn*>(a.v) + base_tok + col0;
     TIn* go = a.o ? reinterpret_cast<TIn*>(a.o) + base_tok + col0 : nullptr;
     const float* gbeta = a.beta + (long long)b * a.T * a.H + h;
@@ -282,7 +286,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     static_assert(Cfg::oKd + sizeof(OpT) * C * PK - Cfg::oLq < 65536, "immediate offsets");
     KDA_LDS OpT* const pA = lds_pin(sLq + sg * TPS * PK + ch0);      // decay-phase rows of Lq, Lk, Kd
     KDA_LDS OpT* const pKp = lds_pin(sKpT + ch0 * PT + sg * TPS);     // this thread's K'^T entries
-    KDA_LDS float* const pLam = lds_pin(sLam + sg * TPS * DK + ch0);  // this thread's raw log-decay
+    KDA_LDS char* const pLam = lds_pin((KDA_LDS char*)sLam + (sg * TPS * DK + ch0) * LAE);  // own raw decay
     KDA_LDS float* const pTotW = lds_pin(sTot + sg * GPT * DK + ch0); // this segment's decay-group totals
     KDA_LDS float* const pTotR = lds_pin(sTot + ch0);                 // all segments' totals
     KDA_LDS float* const pCh = lds_pin(sE + ch0);                     // sE, sD rows of this thread's quad
@@ -310,9 +314,11 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     const uint32_t boB = (uint32_t)((tid % C) * a.H * sizeof(float));
     const int v_row = tid / VPR, v_off = (tid % VPR) * VEL;
     const uint32_t boV = (uint32_t)((v_row * HD + v_off) * sizeof(TIn));
-    const int d_row = (4 * lane) / DK, d_col = (4 * lane) % DK;   // this lane's 16 bytes of a 1 KiB block
-    const uint32_t boLa = (uint32_t)((d_row * HD + d_col) * sizeof(float));
-    constexpr int D_ROWS = 256 / DK;                               // rows per 1 KiB block
+    constexpr int NDM = C * DK * LAE / 1024;                       // 1 KiB decay-input blocks per chunk
+    constexpr int D_ROWS = 1024 / (DK * LAE);                      // rows per 1 KiB block
+    const int d_row = (16 * lane) / (DK * LAE);                    // this lane's 16 bytes of a block
+    const int d_colb = (16 * lane) % (DK * LAE);
+    const uint32_t boLa = (uint32_t)(d_row * HDL + d_colb);
 
     // ---- prefetch of the next chunk: log-decay straight into LDS, the rest into registers ----
     typename QI::raw pq[TPS], pk[TPS];
@@ -326,15 +332,19 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     auto load_decay = [&](long long c0) {
         if (c0 + C <= t_end) {
 #pragma unroll
-            for (int m = 0; m < NDMA / NW; ++m) {
-                const int gi = wave * (NDMA / NW) + m;
-                lds_dma16(at_byte(gla + (c0 + gi * D_ROWS) * HD, pinned_u(boLa)), (KDA_LDS void*)(sLam + gi * 256));
+            for (int m = 0; m < (NDM + NW - 1) / NW; ++m) {
+                const int gi = m * NW + wave;
+                if (NDM % NW == 0 || gi < NDM)
+                    lds_dma16(reinterpret_cast<const float*>(at_byte(gla + (c0 + gi * D_ROWS) * HDL, pinned_u(boLa))),
+                              (KDA_LDS void*)(sLam + gi * 256));
             }
         } else {
 #pragma unroll
-            for (int m = 0; m < NDMA / NW; ++m) {
-                const int gi = wave * (NDMA / NW) + m;
-                lds_dma16(gla + clampt(c0 + gi * D_ROWS + d_row) * HD + d_col, (KDA_LDS void*)(sLam + gi * 256));
+            for (int m = 0; m < (NDM + NW - 1) / NW; ++m) {
+                const int gi = m * NW + wave;
+                if (NDM % NW == 0 || gi < NDM)
+                    lds_dma16(reinterpret_cast<const float*>(gla + clampt(c0 + gi * D_ROWS + d_row) * HDL + d_colb),
+                              (KDA_LDS void*)(sLam + gi * 256));
             }
         }
     };
@@ -408,7 +418,19 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
             float run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
-                const f32x4_t l4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pLam + i * DK);
+                f32x4_t l4;
+                if constexpr (GATE) {
+                    // log alpha = -5 sigmoid(x) = -5 / (1 + 2^{-x log2 e})
+                    const u32x2_t xr = *reinterpret_cast<const KDA_LDS u32x2_t*>(pLam + i * DK * LAE);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t w = u < 2 ? xr[0] : xr[1];
+                        const float x = __uint_as_float((u & 1) ? (w & 0xffff0000u) : (w << 16));
+                        l4[u] = kLogAlphaMin * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
+                    }
+                } else {
+                    l4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pLam + i * DK * LAE);
+                }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float l2 = okt[i] ? fminf(fmaxf(l4[u], kLogAlphaMin), 0.0f) * kLog2e : 0.0f;
@@ -804,13 +826,13 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     }
 }
 
-template <class Cfg, bool DUAL = false>
+template <class Cfg, bool DUAL = false, bool GATE = false>
 hipError_t launch_prefill_cfg(const PrefillArgs& a, hipStream_t stream) {
     const long long groups = ((long long)a.n_units + 7) / 8;
     const long long nblk = groups * 8 * a.n_vs;
     if (nblk <= 0) return hipSuccess;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((kda_prefill_kernel<Cfg, DUAL>), dim3((unsigned)nblk), dim3(Cfg::NTH), 0, stream, a);
+    hipLaunchKernelGGL((kda_prefill_kernel<Cfg, DUAL, GATE>), dim3((unsigned)nblk), dim3(Cfg::NTH), 0, stream, a);
     return hipGetLastError();
 }
 

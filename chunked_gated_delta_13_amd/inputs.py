@@ -190,3 +190,11 @@ def make_spec_inputs(N, m, H, dk, dv, dtype="bf16", decay="sig2", seed=0, device
     acc = torch.randint(0, m + 1, (N,), generator=gen, device=device, dtype=torch.int64)
     return {"q": d["q"], "k": d["k"], "v": d["v"], "log_alpha": d["log_alpha"], "beta": d["beta"],
             "accepted": acc.to(torch.int32).contiguous()}
+
+
+def make_gate(B, T, H, dk, dtype="bf16", seed=0, device="cpu"):
+    """Raw gate pre-activation x ~ N(0, 2) (standard deviation 2), cast to the input dtype, so
+    that -5 * sigmoid(x) has the distribution of the "sig2" log-decay recipe."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) + 104729)
+    return (2.0 * _normal((B, T, H, dk), gen, device)).to(torch_dtype(dtype)).contiguous()

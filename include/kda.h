@@ -153,6 +153,27 @@ kda_status_t kda_chunk_prefill_ckpt(const void *q, const void *k, const void *v,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_prefill_ex with the bounded gate fused: the decay input is the raw gate
+ * pre-activation x (bf16) and log alpha = -5 * sigmoid(x) is formed on load, which moves 2
+ * instead of 4 bytes per key channel and token.  Pages: "Inside Kimi K3" (academa.ai lecture),
+ * sequence paragraph (the decay curve itself is changed so that it is bounded below at -5);
+ * "Kimi K3's architecture" (orkas.ai), "A lower bound that deleted a GPU code path" (the
+ * activation has to be bounded below).  The pages do not print the curve; -5 * sigmoid is the
+ * reading used, the one the benchmark workloads draw log alpha from.
+ *
+ *   gate       [B, T, H, dk]  bf16   raw gate pre-activation (in place of log_alpha)
+ * Other arguments, plans, workspace and errors as for kda_chunk_prefill_ex.  Supported for
+ * dtype KDA_BF16 with dk == dv == 128 (one column slice; n_vs must be 0 or 1); other shapes
+ * return KDA_ERR_UNSUPPORTED.
+ */
+kda_status_t kda_chunk_prefill_gate(const void *q, const void *k, const void *v,
+                                    const void *gate, const float *beta, const float *S0,
+                                    void *o, float *S_T,
+                                    int B, int T, int H, int dk, int dv, int chunk,
+                                    kda_dtype_t dtype, int seg_len, int n_vs,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One decode step for N independent sequences: exactly one token of the
  * recurrence, with the state read and written in place.  Pages: "Inside Kimi
  * K3", sequence paragraph (constant cost per new token); "Kimi K3's

@@ -175,3 +175,27 @@ def prefill_ckpt(q, k, v, log_alpha, beta, S0, ckpt_every, nthreads: int | None 
         if i < n:
             ck[:, i] = s
     return o, s, ck
+
+
+def gate_log_alpha(gate):
+    """The bounded decay curve log alpha = -5 * sigmoid(x) of a raw gate pre-activation x, in
+    float64 (written as -5 / (1 + exp(-x)), stable for large |x|).
+
+    Sources: "Inside Kimi K3" (academa.ai lecture), sequence paragraph: the decay curve itself is
+    changed so that the log-decay is bounded below at -5; "Kimi K3's architecture" (orkas.ai),
+    section "A lower bound that deleted a GPU code path": the activation has to be bounded
+    below.  The pages do not print the curve; -5 * sigmoid is the reading used, the one the
+    benchmark workloads draw log alpha from.
+    """
+    x = _f64(gate)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = -5.0 / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    out[~pos] = -5.0 * e / (1.0 + e)
+    return out
+
+
+def prefill_gate(q, k, v, gate, beta, S0=None, nthreads: int | None = None):
+    """The recurrence with the fused bounded gate: log alpha = gate_log_alpha(gate)."""
+    return prefill(q, k, v, gate_log_alpha(gate), beta, S0, nthreads=nthreads)

@@ -245,3 +245,20 @@ def test_ckpt_validation(lib, host_only):
     assert _ckpt(lib, S_ckpt=None) == INVALID         # T >= every needs the buffer
     assert _ckpt(lib, S_ckpt=_ptrs(8) + 4) == INVALID  # misaligned
     assert _ckpt(lib, S_ckpt=_ptrs(2) + 256) == INVALID   # over v
+
+
+def _gate(lib, dt=BF16, dk=128, gate=_ptrs(3), nvs=0, **kw):
+    args = _ok_ptrs()
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return lib.kda_chunk_prefill_gate(vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(gate), vp(args["beta"]),
+                                      None, vp(args["o"]), None, 2, 1000, 3, dk, dk, 64 if dt == BF16 else 32,
+                                      dt, 0, nvs, None, 0, None)
+
+
+def test_gate_validation(lib, host_only):
+    assert _gate(lib, dt=F32) == UNSUPPORTED
+    assert _gate(lib, dk=64) == UNSUPPORTED
+    assert _gate(lib, nvs=2) == UNSUPPORTED
+    assert _gate(lib, gate=None) == INVALID
+    assert _gate(lib, gate=_ptrs(3) + 2) == INVALID
