@@ -24,6 +24,7 @@ using kda::PrefillArgs;
 
 constexpr long long kMinSegTokens = 4096;   // shortest segment worth a transition pass
 constexpr int kDefaultWaves = 8;            // waves per workgroup for 128-column bf16 slices
+constexpr int kDualChunk = 64;              // longest chunk of the shared transition/increment pass
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -427,7 +428,16 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     pm.seg0 = 0;
     pm.n_seg_launch = ns - 1;
     pm.n_units = (int)(bh * (ns - 1));
-    if (kda::prefill_dual_supported(dk, dvw, chunk, f32)) {
+    // The shared transition/increment pass may use another chunk than the output pass (M_s and
+    // H_s do not depend on it beyond rounding).  It uses the caller's chunk: at 64 tokens the two
+    // states spill a few registers outside the chunk loop, and the pass is still faster than at
+    // 32.  KDA_DUAL_CHUNK overrides (tuning only).
+    int dchunk = chunk > kDualChunk ? kDualChunk : chunk;
+    if (const char* e = getenv("KDA_DUAL_CHUNK")) {
+        const int v = atoi(e);
+        if ((v == 16 || v == 32 || v == 64) && sl % v == 0) dchunk = v;
+    }
+    if (kda::prefill_dual_supported(dk, dvw, dchunk, f32)) {
         PrefillArgs pd = pm;  // M_s and H_s together: the decay and intra-chunk work is shared
         pd.init_mode = 0;
         pd.zero_values = 0;
@@ -435,7 +445,7 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
         pd.s_aux = wsM;
         pd.saux_bh_stride = pm.sout_bh_stride;
         pd.saux_seg_stride = pm.sout_seg_stride;
-        if (kda::launch_prefill_dual(dk, dvw, chunk, f32, pd, s) != hipSuccess) return KDA_ERR_DEVICE;
+        if (kda::launch_prefill_dual(dk, dvw, dchunk, f32, pd, s) != hipSuccess) return KDA_ERR_DEVICE;
     } else {
         if (kda::launch_prefill(dk, dvw, chunk, f32, pm, s) != hipSuccess) return KDA_ERR_DEVICE;
         PrefillArgs ph = pm;  // H_s: zero start, real values, no output

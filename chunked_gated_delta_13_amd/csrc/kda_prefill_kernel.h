@@ -96,7 +96,7 @@ struct PrefillCfg {
     static constexpr size_t oTot = oBeta + al(4 * C);
     static constexpr size_t oO = oTot + al(4 * 16 * DK);
     static constexpr size_t LDS = oO + al(sizeof(TIn) * NW * 16 * PW);
-    static_assert(LDS + 4 * C * DK <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    static_assert(LDS <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 
 // Row tile of the pi-th (row, column <= row) tile pair, pairs enumerated row by row.
@@ -178,10 +178,6 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     KDA_LDS float* sBeta = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oBeta);
     KDA_LDS float* sTot = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oTot);
     KDA_LDS TIn* sO = reinterpret_cast<KDA_LDS TIn*>(smem + Cfg::oO);
-    // raw log-decay of the next chunk, written by direct global->LDS loads; a separate object so
-    // that the compiler can tell those writes never alias the arrays above
-    __shared__ __align__(16) float sLam_[C * DK];
-    KDA_LDS float* sLam = (KDA_LDS float*)sLam_;
 
     // ---- unit of this workgroup; sibling column slices share an XCD (blockIdx % 8) ----
     const int bid = blockIdx.x;
@@ -286,7 +282,6 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     static_assert(Cfg::oKd + sizeof(OpT) * C * PK - Cfg::oLq < 65536, "immediate offsets");
     KDA_LDS OpT* const pA = lds_pin(sLq + sg * TPS * PK + ch0);      // decay-phase rows of Lq, Lk, Kd
     KDA_LDS OpT* const pKp = lds_pin(sKpT + ch0 * PT + sg * TPS);     // this thread's K'^T entries
-    KDA_LDS char* const pLam = lds_pin((KDA_LDS char*)sLam + (sg * TPS * DK + ch0) * LAE);  // own raw decay
     KDA_LDS float* const pTotW = lds_pin(sTot + sg * GPT * DK + ch0); // this segment's decay-group totals
     KDA_LDS float* const pTotR = lds_pin(sTot + ch0);                 // all segments' totals
     KDA_LDS float* const pCh = lds_pin(sE + ch0);                     // sE, sD rows of this thread's quad
@@ -314,14 +309,13 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     const uint32_t boB = (uint32_t)((tid % C) * a.H * sizeof(float));
     const int v_row = tid / VPR, v_off = (tid % VPR) * VEL;
     const uint32_t boV = (uint32_t)((v_row * HD + v_off) * sizeof(TIn));
-    constexpr int NDM = C * DK * LAE / 1024;                       // 1 KiB decay-input blocks per chunk
-    constexpr int D_ROWS = 1024 / (DK * LAE);                      // rows per 1 KiB block
-    const int d_row = (16 * lane) / (DK * LAE);                    // this lane's 16 bytes of a block
-    const int d_colb = (16 * lane) % (DK * LAE);
-    const uint32_t boLa = (uint32_t)(d_row * HDL + d_colb);
+    const uint32_t boLa = (uint32_t)((sg * TPS) * HDL + ch0 * LAE);
 
-    // ---- prefetch of the next chunk: log-decay straight into LDS, the rest into registers ----
+    // ---- prefetch of the next chunk into registers: the decay input, q and k in the layout the
+    //      decay phase uses (TPS tokens x one channel quad per thread), v and beta ----
+    using LaRaw = std::conditional_t<GATE, u32x2_t, f32x4_t>;
     typename QI::raw pq[TPS], pk[TPS];
+    LaRaw pla[TPS];
     float pbeta = 0.0f;
     u32x4_t pv[NVV];
     auto clampt = [&](long long t) { return t < t_end ? t : t_end - 1; };
@@ -329,32 +323,37 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     // Loads only: in a partial last chunk, rows past the end of the unit read the last valid row
     // (in bounds) and are zeroed when the chunk is consumed, so no select waits on a load in
     // flight.  A zero key, value, query, beta and log-decay is an exact identity on the state.
-    auto load_decay = [&](long long c0) {
-        if (c0 + C <= t_end) {
-#pragma unroll
-            for (int m = 0; m < (NDM + NW - 1) / NW; ++m) {
-                const int gi = m * NW + wave;
-                if (NDM % NW == 0 || gi < NDM)
-                    lds_dma16(reinterpret_cast<const float*>(at_byte(gla + (c0 + gi * D_ROWS) * HDL, pinned_u(boLa))),
-                              (KDA_LDS void*)(sLam + gi * 256));
-            }
-        } else {
-#pragma unroll
-            for (int m = 0; m < (NDM + NW - 1) / NW; ++m) {
-                const int gi = m * NW + wave;
-                if (NDM % NW == 0 || gi < NDM)
-                    lds_dma16(reinterpret_cast<const float*>(gla + clampt(c0 + gi * D_ROWS + d_row) * HDL + d_colb),
-                              (KDA_LDS void*)(sLam + gi * 256));
-            }
-        }
-    };
-    auto load_rest = [&](long long c0) {
+    // q, k and the decay input: consumed by the decay phases A and A'
+    auto load_qk = [&](long long c0) {
         if (c0 + C <= t_end) {
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
+                pla[i] = *reinterpret_cast<const LaRaw*>(at_byte(gla + (c0 + i) * HDL, pinned_u(boLa)));
                 if constexpr (!DUAL) pq[i] = QI::load(at_byte(gq + (c0 + i) * HD, pinned_u(boQK)));
                 pk[i] = QI::load(at_byte(gk + (c0 + i) * HD, pinned_u(boQK)));
             }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TPS; ++i) {
+                const long long t = clampt(c0 + sg * TPS + i);
+                const long long off = t * HD + ch0;
+                pla[i] = *reinterpret_cast<const LaRaw*>(gla + t * HDL + ch0 * LAE);
+                if constexpr (!DUAL) pq[i] = QI::load(gq + off);
+                pk[i] = QI::load(gk + off);
+            }
+            // rows past the end act as zero queries and keys (their decay is masked in phase A);
+            // this path runs at most once per unit, so the wait these selects imply costs nothing
+#pragma unroll
+            for (int i = 0; i < TPS; ++i)
+                if (c0 + sg * TPS + i >= t_end) {
+                    if constexpr (!DUAL) pq[i] = QI::zero();
+                    pk[i] = QI::zero();
+                }
+        }
+    };
+    // v and beta: consumed when phase A commits them to LDS
+    auto load_vb = [&](long long c0) {
+        if (c0 + C <= t_end) {
             pbeta = *at_byte(gbeta + c0 * a.H, pinned_u(boB));
             // values are fetched even when a pass ignores them: a conditional load would make the
             // compiler wait for it where the two paths merge
@@ -363,20 +362,6 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 if (NV % NTH == 0 || tid + NTH * m < NV)
                     pv[m] = *reinterpret_cast<const u32x4_t*>(at_byte(gv + (c0 + m * (NTH / VPR)) * HD, pinned_u(boV)));
         } else {
-#pragma unroll
-            for (int i = 0; i < TPS; ++i) {
-                const long long off = clampt(c0 + sg * TPS + i) * HD + ch0;
-                if constexpr (!DUAL) pq[i] = QI::load(gq + off);
-                pk[i] = QI::load(gk + off);
-            }
-            // rows past the end act as zero queries and keys; this path runs at most once per
-            // unit, so the wait these selects imply costs nothing
-#pragma unroll
-            for (int i = 0; i < TPS; ++i)
-                if (c0 + sg * TPS + i >= t_end) {
-                    if constexpr (!DUAL) pq[i] = QI::zero();
-                    pk[i] = QI::zero();
-                }
             pbeta = gbeta[clampt(c0 + (tid % C)) * a.H];
 #pragma unroll
             for (int m = 0; m < NVV; ++m)
@@ -388,8 +373,8 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     const long long ntok = t_end - t_begin;
     const int nchunks = ntok > 0 ? (int)((ntok + C - 1) / C) : 0;
     if (nchunks > 0) {
-        load_decay(t_begin);
-        load_rest(t_begin);
+        load_qk(t_begin);
+        load_vb(t_begin);
     }
 
     for (int c = 0; c < nchunks; ++c) {
@@ -421,7 +406,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 f32x4_t l4;
                 if constexpr (GATE) {
                     // log alpha = -5 sigmoid(x) = -5 / (1 + 2^{-x log2 e})
-                    const u32x2_t xr = *reinterpret_cast<const KDA_LDS u32x2_t*>(pLam + i * DK * LAE);
+                    const u32x2_t xr = pla[i];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const uint32_t w = u < 2 ? xr[0] : xr[1];
@@ -429,7 +414,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                         l4[u] = kLogAlphaMin * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
                     }
                 } else {
-                    l4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pLam + i * DK * LAE);
+                    l4 = pla[i];
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -442,8 +427,6 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
             }
         }
         barrier_lds();
-        // the raw log-decay of this chunk is consumed: fetch the next chunk's behind everything below
-        if (c + 1 < nchunks) load_decay(c0 + C);
 
         // ================= A': references and decay-scaled operands =================
         {
@@ -534,8 +517,8 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
 #pragma unroll
             for (int u = 0; u < 4; ++u) lds_store_run<TPS>(pKp + u * PT, kp[u]);
         }
-        // the raw q, k, v of this chunk are consumed: fetch the next chunk's
-        if (c + 1 < nchunks) load_rest(c0 + C);
+        // this chunk's q, k and decay input are consumed: fetch the next chunk's
+        if (c + 1 < nchunks) load_qk(c0 + C);
         barrier_lds();
 
         // ================= B: decay-weighted KK^T and QK^T tiles =================
@@ -592,6 +575,10 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
             });
         }
         barrier_lds();
+
+        // v and beta of this chunk were committed in phase A: fetch the next chunk's (issued here so
+        // that the workgroup's loads do not all queue at the same point of the chunk)
+        if (c + 1 < nchunks) load_vb(c0 + C);
 
         // ====== C: diagonal blocks T_aa = (I + A_aa)^{-1} on wave 0; K~, Q~ formed in place ======
         if (wave == 0) {

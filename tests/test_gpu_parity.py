@@ -180,14 +180,17 @@ def test_prefill_column_split_matches_unsplit():
 
 def test_prefill_split_one_pass_matches_two_pass():
     """With one column slice the transitions and increments come from one shared pass; with two
-    slices from two separate passes.  Columns are independent, so both give the same bits."""
+    slices from two separate passes.  Both match the oracle and each other to the bf16
+    tolerance (the shared pass may run a different chunk length)."""
     inp = _case(1, 900, 2, 128, "bf16", decay="slow", s0=1.0, seed=29)
     o1, s1 = _run_prefill(inp, 64, seg_len=192, n_vs=1)
     o2, s2 = _run_prefill(inp, 64, seg_len=192, n_vs=2)
-    assert torch.equal(o1, o2) and torch.equal(s1, s2)
     o_ref, s_ref = _oracle(inp)
-    assert_close("o", o1, o_ref, "bf16")
-    assert_close("S_T", s1, s_ref, "bf16")
+    assert_close("o one pass", o1, o_ref, "bf16")
+    assert_close("S_T one pass", s1, s_ref, "bf16")
+    assert_close("o two passes", o2, o_ref, "bf16")
+    assert_close("o one vs two passes", o1, to_f64(o2), "bf16")
+    assert_close("S_T one vs two passes", s1, to_f64(s2), "bf16")
 
 
 def test_prefill_in_place_state():
