@@ -183,6 +183,11 @@ template <typename T> __device__ __forceinline__ KDA_LDS T* lds_pin(KDA_LDS T* p
     asm volatile("" : "+v"(x));
     return (KDA_LDS T*)(size_t)x;
 }
+// Value of x in lane I of this lane's 16-lane row (DPP row broadcast).
+template <int I> __device__ __forceinline__ float row_bcast(float x) {
+    static_assert(I >= 0 && I < 16, "row lane");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + I, 0xF, 0xF, false));
+}
 __device__ __forceinline__ int pinned(int x) {
     asm volatile("" : "+v"(x));
     return x;

@@ -78,8 +78,7 @@ struct PrefillCfg {
     static_assert(TPS % G == 0, "segment holds whole decay groups");
     static_assert(DK % 32 == 0 && C % 16 == 0 && NT <= 4, "shape");
     static_assert(NTH % VPR == 0, "value rows split evenly over the threads");
-    static constexpr int CV_ROWS = (NTH - 64) / (DK / 4);       // rows per in-place scaling step
-    static_assert((NTH - 64) % (DK / 4) == 0, "in-place scaling covers whole rows");
+    static_assert(NT <= NW, "one wave per diagonal block");
 
     static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t oLq = 0;
@@ -131,6 +130,14 @@ template <> struct Quad<__bf16> {
         v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
         *reinterpret_cast<KDA_LDS bf16x4_t*>(p) = v;
     }
+    __device__ __forceinline__ static raw pack(float a, float b, float c, float d) {
+        bf16x4_t v;
+        v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+        return __builtin_bit_cast(raw, v);
+    }
+    __device__ __forceinline__ static void store_raw(KDA_LDS __bf16* p, raw r) {
+        *reinterpret_cast<KDA_LDS u32x2_t*>(p) = r;
+    }
 };
 template <> struct Quad<float> {
     typedef f32x4_t raw;
@@ -140,6 +147,10 @@ template <> struct Quad<float> {
     __device__ __forceinline__ static float get(raw r, int i) { return r[i]; }
     __device__ __forceinline__ static void store(KDA_LDS float* p, float a, float b, float c, float d) {
         *reinterpret_cast<KDA_LDS f32x4_t*>(p) = f32x4_t{a, b, c, d};
+    }
+    __device__ __forceinline__ static raw pack(float a, float b, float c, float d) { return f32x4_t{a, b, c, d}; }
+    __device__ __forceinline__ static void store_raw(KDA_LDS float* p, raw r) {
+        *reinterpret_cast<KDA_LDS f32x4_t*>(p) = r;
     }
 };
 
@@ -159,7 +170,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     constexpr int SPT = Cfg::SPT, G = Cfg::G, GPT = Cfg::GPT, PK = Cfg::PK, PT = Cfg::PT, PV = Cfg::PV, PW = Cfg::PW;
     constexpr int PD = Cfg::PD, PDB = Cfg::PDB, VEL = Cfg::VEL, VPR = Cfg::VPR, NV = Cfg::NV, NVV = Cfg::NVV;
     constexpr int VPRW = Cfg::VPRW, NOT = Cfg::NOT, NOTL = Cfg::NOTL;
-    constexpr int NQT = Cfg::NQT, NW = Cfg::NW, NTH = Cfg::NTH, CV_ROWS = Cfg::CV_ROWS;
+    constexpr int NQT = Cfg::NQT, NW = Cfg::NW, NTH = Cfg::NTH;
     constexpr int NIT = DK / 16;   // 16-row tiles of the state
     constexpr int NKB = DK / 32;   // 32-channel contraction blocks
 
@@ -290,16 +301,13 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     KDA_LDS OpT* const pT = lds_pin(sKpT + lr * PT + 4 * lg);         // fragment rows of KpT, TA, B
     KDA_LDS float* const pG = lds_pin(sE + 4 * lg);                   // sE, sD, sBeta by accumulator row
     KDA_LDS OpT* const pW = lds_pin(sTA + 4 * lg * PT + lr);          // accumulator element of TA, B
-    KDA_LDS float* const pAd = lds_pin(sAd + lr * PD + 4 * lg);       // transposed diagonal-block store
-    KDA_LDS float* const pAdT = lds_pin(sAd + (lane >> 4) * PDB);     // diagonal block of this lane (wave 0)
-    KDA_LDS OpT* const pE1 = lds_pin(sTA + (lane >> 4) * 16 * (PT + 1) + (lane & 15));  // T_aa column (wave 0)
+    KDA_LDS float* const pAd = lds_pin(sAd + 4 * lg * PD + lr);       // diagonal-block store, row-major
+    // diagonal-block inverse (wave a inverts block a): lane = (column group lane / 16, row lane % 16)
+    KDA_LDS float* const pAi = lds_pin(sAd + wave * PDB + (lane & 15) * PD);   // row of A_aa
+    KDA_LDS OpT* const pTi = lds_pin(sTA + 16 * wave * (PT + 1) + (lane & 15) * PT + (lane >> 4));
     KDA_LDS TIn* const pV = lds_pin(sV + 4 * lg * PV + wave * 16 * NCT + lr);  // value in accumulator layout
     KDA_LDS TIn* const pOw = lds_pin(sO + wave * 16 * PW + 4 * lg * PW + lr);  // output staging write
     KDA_LDS TIn* const pOr = lds_pin(sO + wave * 16 * PW + (lane / VPRW) * PW + (lane % VPRW) * VEL);
-    const int tq = tid - 64;                                          // waves 1..NW-1: in-place scaling
-    const int cvRow0 = tq / (DK / 4);
-    KDA_LDS OpT* const pCv = lds_pin(sLq + cvRow0 * PK + 4 * (tq % (DK / 4)));
-    KDA_LDS float* const pCe = lds_pin(sE + 4 * (tq % (DK / 4)));
     // byte offset of this lane's output vector from the uniform row base
     const uint32_t boGo = (uint32_t)(((lane / VPRW) * HD + wave * 16 * NCT + (lane % VPRW) * VEL) * sizeof(TIn));
 
@@ -429,6 +437,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
         barrier_lds();
 
         // ================= A': references and decay-scaled operands =================
+        typename QO::raw qtr[TPS], ktr[TPS];   // Q~, K~ of this thread's rows, stored after phase B
         {
             // One summation order for every thread layout: group totals in order inside each
             // 16-token tile, tile totals in order across the chunk.  Rt[a] = rho_a.
@@ -495,17 +504,26 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 }
             }
             float kp[4][TPS];   // K' of this thread's channels, by channel: one vector store each
+            float er[4];        // 2^{rho_a} of this thread's channels (<= 1)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) er[u] = fast_exp2(rho[u]);
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
-                float lq[4], lk[4], kd[4];
+                float lq[4], lk[4], kd[4], qt[4], kt[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float loc = gp[i / G][u] + g[i][u];   // g - rho_a, in [-115.4, 0]
                     const float x = fast_exp2(loc);              // <= 1
                     const float y = fast_exp2(-loc);             // >= 1, at most 2^115.4 = e^80
                     const float kv = QI::get(pk[i], u);
-                    if constexpr (!DUAL) lq[u] = QI::get(pq[i], u) * x;
+                    const float xe = x * er[u];                  // 2^{g} <= 1
+                    if constexpr (!DUAL) {
+                        const float qv = QI::get(pq[i], u);
+                        lq[u] = qv * x;
+                        qt[u] = qv * xe;
+                    }
                     lk[u] = kv * x;
+                    kt[u] = kv * xe;
                     kd[u] = kv * y;
                     // K' = k 2^{g_C - g}: the factor above 1 meets only a factor that cannot underflow
                     kp[u][i] = (kd[u] * fd[u]) * fc[u];
@@ -513,6 +531,10 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 if constexpr (!DUAL) QO::store(pA + i * PK, lq[0], lq[1], lq[2], lq[3]);
                 QO::store(pA + eLk + i * PK, lk[0], lk[1], lk[2], lk[3]);
                 QO::store(pA + eKd + i * PK, kd[0], kd[1], kd[2], kd[3]);
+                // K~ = k 2^{g}, Q~ = q 2^{g}: kept in registers and written over Lk, Lq once the
+                // tile pairs have read those
+                if constexpr (!DUAL) qtr[i] = QO::pack(qt[0], qt[1], qt[2], qt[3]);
+                ktr[i] = QO::pack(kt[0], kt[1], kt[2], kt[3]);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) lds_store_run<TPS>(pKp + u * PT, kp[u]);
@@ -564,7 +586,8 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                         ad[j] = (lr < rl) ? accA[j] * bt4[j] : 0.0f;
                         if constexpr (!DUAL) pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
                     }
-                    *reinterpret_cast<KDA_LDS f32x4_t*>(pAd + ar * PDB) = ad;  // transposed
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) pAd[ar * PDB + j * PD] = ad[j];
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -580,58 +603,33 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
         // that the workgroup's loads do not all queue at the same point of the chunk)
         if (c + 1 < nchunks) load_vb(c0 + C);
 
-        // ====== C: diagonal blocks T_aa = (I + A_aa)^{-1} on wave 0; K~, Q~ formed in place ======
-        if (wave == 0) {
-            if ((lane >> 4) < NT) {
-                // column (lane & 15) of T_aa by right-looking forward substitution; A_aa read by columns
-                const int jj = lane & 15;
-                float col[16];
+        // ====== C: K~, Q~ over Lk, Lq; diagonal blocks T_aa = (I + A_aa)^{-1} ======
 #pragma unroll
-                for (int r = 0; r < 16; ++r) col[r] = (r == jj) ? 1.0f : 0.0f;
-                // column i of A_aa (only the quads below the diagonal), fetched two steps ahead
-                f32x4_t acol[15][4];
-                auto fetch = [&](auto I) {
-                    constexpr int i = decltype(I)::value;
+        for (int i = 0; i < TPS; ++i) {
+            if constexpr (!DUAL) QO::store_raw(pA + i * PK, qtr[i]);
+            QO::store_raw(pA + eLk + i * PK, ktr[i]);
+        }
+        if (wave < NT) {
+            // wave a inverts diagonal block a by right-looking forward substitution: lane (cgp, p)
+            // holds rows p of columns j = cgp + 4 r of T_aa; the pivot row i of each column is
+            // broadcast inside the 16-lane row by DPP, so no step waits on LDS
+            const int p = lane & 15, cgp = lane >> 4;
+            float na[16];   // -A_aa[p][i]
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        if (4 * q4 + 3 > i) acol[i][q4] = *reinterpret_cast<const KDA_LDS f32x4_t*>(pAdT + i * PD + 4 * q4);
-                };
-                fetch(std::integral_constant<int, 0>{});
-                fetch(std::integral_constant<int, 1>{});
-                static_for<0, 15>([&](auto I) {
-                    constexpr int i = decltype(I)::value;
-                    if constexpr (i + 2 < 15) fetch(std::integral_constant<int, i + 2>{});
-#pragma unroll
-                    for (int r = i + 1; r < 16; ++r) col[r] -= acol[i][r / 4][r % 4] * col[i];
-                });
-#pragma unroll
-                for (int r = 0; r < 16; ++r) pE1[r * PT] = from_f32<OpT>(col[r]);
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4_t v4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pAi + 4 * q4);
+                na[4 * q4] = -v4[0]; na[4 * q4 + 1] = -v4[1]; na[4 * q4 + 2] = -v4[2]; na[4 * q4 + 3] = -v4[3];
             }
-        } else {
-            // K~ = Lk 2^{rho_a}, Q~ = Lq 2^{rho_a} (factors <= 1), in place; all loads issued first
-            constexpr int NARR = DUAL ? 1 : 2;
-            constexpr int NM = (C + CV_ROWS - 1) / CV_ROWS;
-            typename QO::raw x[NARR][NM];
-            f32x4_t e4[NM];
+            float t[4];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                if (cvRow0 + m * CV_ROWS < C) {
-                    e4[m] = *reinterpret_cast<const KDA_LDS f32x4_t*>(pCe + ((cvRow0 + m * CV_ROWS) >> 4) * DK);
+            for (int r = 0; r < 4; ++r) t[r] = (p == cgp + 4 * r) ? 1.0f : 0.0f;
+            static_for<0, 15>([&](auto I) {
+                constexpr int i = decltype(I)::value;
 #pragma unroll
-                    for (int arr = 0; arr < NARR; ++arr)
-                        x[arr][m] = QO::load((arr ? pCv : pCv + eLk) + m * CV_ROWS * PK);
-                }
-            }
+                for (int r = 0; r < 4; ++r) t[r] = fmaf(na[i], row_bcast<i>(t[r]), t[r]);
+            });
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                if (cvRow0 + m * CV_ROWS < C) {
-#pragma unroll
-                    for (int arr = 0; arr < NARR; ++arr)
-                        QO::store((arr ? pCv : pCv + eLk) + m * CV_ROWS * PK, QO::get(x[arr][m], 0) * e4[m][0],
-                                  QO::get(x[arr][m], 1) * e4[m][1], QO::get(x[arr][m], 2) * e4[m][2],
-                                  QO::get(x[arr][m], 3) * e4[m][3]);
-                }
-            }
+            for (int r = 0; r < 4; ++r) pTi[4 * r] = from_f32<OpT>(t[r]);
         }
         barrier_lds();
 
