@@ -299,8 +299,11 @@ def cpu_baseline(gen_inputs, w, budget_s=15.0):
 
 
 def prefill_kernel_name() -> str:
-    """Instantiation that runs the model-width workload (one 128-column slice per workgroup)."""
+    """Kernel that runs the model-width workload (one 128-column slice per workgroup)."""
     nw = 4 if os.environ.get("KDA_PREFILL_WAVES") == "4" else 8
+    pipe = os.environ.get("KDA_PREFILL_PIPE", "8")
+    if nw == 8 and pipe in ("4", "8"):
+        return f"kda_prefill_pipe_kernel<{pipe},false>"
     return f"kda_prefill_kernel<PrefillCfg<128,{8 // nw},64,bf16,{nw}>>"
 
 

@@ -14,6 +14,7 @@ namespace kda {
 hipError_t launch_prefill_bf16(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16_dual(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16_pipe(int ncw, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16_gate(int dk, int dvw, int nw, int chunk, bool dual, const PrefillArgs& a,
                                     hipStream_t s);
 }  // namespace kda
@@ -24,6 +25,7 @@ using kda::PrefillArgs;
 
 constexpr long long kMinSegTokens = 4096;   // shortest segment worth a transition pass
 constexpr int kDefaultWaves = 8;            // waves per workgroup for 128-column bf16 slices
+constexpr int kDefaultPipeChunkWaves = 8;   // chunk waves of the two-role prefill kernel
 constexpr int kDualChunk = 64;              // longest chunk of the shared transition/increment pass
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -205,8 +207,25 @@ int prefill_waves(int dk, int dvw, bool f32) {
     return cached;
 }
 
+// Chunk waves of the two-role look-ahead kernel (4 or 8), or 0 when a launch does not run on it.
+// It takes bf16, d_k = d_v = 128 in one slice, 64-token chunks, no per-sequence lengths and real
+// values.  KDA_PREFILL_PIPE=0 keeps such launches on the single-role kernel and
+// KDA_PREFILL_PIPE=4 or 8 picks the chunk waves (tuning and cross-checks only).
+static int pipe_chunk_waves(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a) {
+    static int ncw = -1;
+    if (ncw < 0) {
+        const char* e = getenv("KDA_PREFILL_PIPE");
+        const int v = e ? atoi(e) : kDefaultPipeChunkWaves;
+        ncw = (v == 0 || v == 4 || v == 8) ? v : kDefaultPipeChunkWaves;
+    }
+    const bool fits = !f32 && dk == 128 && dvw == 128 && chunk == 64 && a.n_vs == 1 && !a.lens &&
+                      !a.zero_values && prefill_waves(dk, dvw, f32) == 8;
+    return fits ? ncw : 0;
+}
+
 hipError_t launch_prefill(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a, hipStream_t s) {
     if (!prefill_supported(dk, dvw, chunk, f32)) return hipErrorInvalidValue;
+    if (const int ncw = pipe_chunk_waves(dk, dvw, chunk, f32, a)) return launch_prefill_bf16_pipe(ncw, a, s);
     const int nw = prefill_waves(dk, dvw, f32);
     if (a.gate) return f32 ? hipErrorInvalidValue : launch_prefill_bf16_gate(dk, dvw, nw, chunk, false, a, s);
     return f32 ? launch_prefill_f32(dk, dvw, nw, chunk, a, s) : launch_prefill_bf16(dk, dvw, nw, chunk, a, s);

@@ -188,6 +188,9 @@ template <int I> __device__ __forceinline__ float row_bcast(float x) {
     static_assert(I >= 0 && I < 16, "row lane");
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + I, 0xF, 0xF, false));
 }
+// Marks a register value as redefined at this point: computation that reads it cannot be moved
+// above here (a load into it is waited for here, not earlier).
+template <typename T> __device__ __forceinline__ void reg_pin(T& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ int pinned(int x) {
     asm volatile("" : "+v"(x));
     return x;

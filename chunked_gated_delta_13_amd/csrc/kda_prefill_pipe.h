@@ -1,0 +1,767 @@
+// Two-role chunked KDA prefill for gfx950: one chunk of look-ahead.
+//
+// The kernel in kda_prefill_kernel.h runs every phase of a chunk on all of its waves, one after
+// the other, with a workgroup barrier between phases; the state-independent work of a chunk
+// (decay, decay-scaled operands, tile pairs, diagonal inverses: VALU-heavy) and the
+// state-dependent work (state products: matrix cores and LDS) never overlap.  Here the waves of
+// a workgroup take two roles and two chunks are in flight:
+//   NCW "chunk waves" (4 or 8) prepare chunk c+1: phases A, A', B and the diagonal inverses;
+//   4 "state waves" hold the fp32 state, 32 columns each, and run chunk c:
+//   X = K~S and RHS (from the state after chunk c-1), U, O, state update.
+// Every SIMD hosts waves of both roles, so VALU work of one role issues while the other waits on
+// the matrix cores or LDS.  Per loop iteration there are four barrier intervals, the same for
+// both roles:
+//   1: A(c+1)          | U(c)
+//   2: A'(c+1)         | O(c)            chunk waves hand over V, beta of c+1
+//   3: B(c+1)          | state update(c) chunk waves hand over K~, Q~ of c+1
+//   4: inverses(c+1)   | X, RHS(c+1)     chunk waves hand over K'^T, 2^{g_C} of c+1
+// An operand array of chunk c is overwritten for c+1 only in an interval after the last state
+// wave read it, so it needs one copy.  The arithmetic of every phase is that of
+// kda_prefill_kernel.h (same decay summation order, same products); sources as cited there:
+// "Kimi K3" (meridianbulletin.com), "Parallelizing Sequential State Updates"; "Kimi K3's
+// architecture" (orkas.ai), "A lower bound that deleted a GPU code path".
+#pragma once
+
+#include "kda_prefill_kernel.h"
+
+namespace kda {
+
+// Byte sizes rounded up to 16 (LDS arrays start on 16-byte boundaries).
+constexpr size_t pipe_al(size_t x) { return (x + 15) & ~size_t(15); }
+
+template <int NCW_>
+struct PipeCfg {
+    static constexpr int NCW = NCW_;             // chunk waves (4 or 8); the state waves are 4
+    static constexpr int DK = 128;
+    static constexpr int C = 64;
+    static constexpr int NT = C / 16;            // 16-token row tiles
+    static constexpr int NTB = NT / 2;           // 32-token contraction blocks
+    static constexpr int NTH = 64 * (NCW + 4);   // threads per workgroup
+    static constexpr int NCTH = 64 * NCW;        // chunk-wave threads
+    static constexpr int NQ = DK / 4;            // channel quads
+    static constexpr int NSEG = NCTH / NQ;       // token segments of the chunk waves
+    static constexpr int TPS = C / NSEG;         // tokens per segment
+    static constexpr int G = C / 16;             // tokens per decay group
+    static constexpr int GPT = TPS / G;          // decay groups per segment
+    static constexpr int SPT = 16 / G;           // decay groups per tile
+    static constexpr int NCT = 2;                // 16-column tiles per state wave
+    static constexpr int PK = DK + 8;            // pitch of [C][DK] operand arrays
+    static constexpr int PT = C + 8;             // pitch of [*][C] arrays
+    static constexpr int PV = DK + 8;            // pitch of the value rows
+    static constexpr int PD = 20;
+    static constexpr int PDB = 16 * PD + 16;
+    static constexpr int VROWS = NCTH / 16;      // value rows per pass of the chunk threads
+    static constexpr int NVV = C / VROWS;        // 16-byte value vectors per chunk thread
+    // Interval (1..4, at its end) in which the next chunk's decay input, q, k and v + beta are
+    // requested.  Each is requested only after the current chunk's copy is consumed.  Measured
+    // on the model-width workload: requests kept out of interval 2 (where the outputs are
+    // stored and A' runs) and mostly late in the chunk are fastest; the decay input, consumed
+    // first, goes right after phase A.
+    static constexpr int LD_LA = 1;
+    static constexpr int LD_Q = 4;
+    static constexpr int LD_K = 4;
+    static constexpr int LD_VB = NCW == 8 ? 4 : 3;
+
+    // state-wave operands of one chunk (written by the chunk waves, read by the state waves)
+    static constexpr size_t oQt = 0;
+    static constexpr size_t oKt = oQt + pipe_al(2 * C * PK);
+    static constexpr size_t oKpT = oKt + pipe_al(2 * C * PK);
+    static constexpr size_t oTA = oKpT + pipe_al(2 * DK * PT);
+    static constexpr size_t oB = oTA + pipe_al(2 * C * PT);
+    static constexpr size_t oV = oB + pipe_al(2 * C * PT);
+    static constexpr size_t oBeta = oV + pipe_al(2 * C * PV);
+    static constexpr size_t oGam = oBeta + pipe_al(4 * C);
+    // chunk-wave scratch
+    static constexpr size_t oLq = oGam + pipe_al(4 * DK);
+    static constexpr size_t oLk = oLq + pipe_al(2 * C * PK);
+    static constexpr size_t oKd = oLk + pipe_al(2 * C * PK);
+    static constexpr size_t oTot = oKd + pipe_al(2 * C * PK);
+    static constexpr size_t oD = oTot + pipe_al(4 * 16 * DK);
+    static constexpr size_t oAd = oD + pipe_al(4 * NT * DK);
+    static constexpr size_t LDS = oAd + pipe_al(4 * NT * PDB);
+    static_assert(LDS <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    static_assert((NCW == 4 && TPS == 8) || (NCW == 8 && TPS == 4), "segment layout of the chunk waves");
+    static_assert(TPS % G == 0 && NSEG % NT == 0, "segments hold whole decay groups");
+    static_assert(oB + 2 * C * PT - oKpT < 65536 && oKd + 2 * C * PK - oLq < 65536, "immediate offsets");
+};
+
+// Chunk wave that forms the pi-th tile pair: each takes about the same work (diagonal pairs are
+// the cheapest, pairs far below the diagonal the dearest).
+template <int NCW>
+constexpr int pipe_pair_owner(int pi) {
+    constexpr int own4[10] = {0, 2, 3, 1, 2, 3, 0, 1, 3, 2};
+    constexpr int own8[10] = {0, 1, 2, 3, 4, 5, 6, 7, 5, 2};
+    return NCW == 4 ? own4[pi] : own8[pi];
+}
+
+// Unit (sequence b, head h, segment s) of one workgroup and its token range.
+struct PipeUnit {
+    int b, h, s, bh;
+    long long t_begin, t_end;
+    int nchunks;
+    long long HD;          // token stride of every [B, T, H, d] tensor
+    long long base_tok;    // element offset of (b, token 0, h, 0)
+};
+
+// Chunk waves (0 .. NCW-1): for each chunk in order, phases A, A', B and the diagonal inverses
+// (waves 0..3, one block each), handing the state waves every operand they read.  Four barriers
+// per chunk, then four more while the state waves run the last chunk.
+template <int NCW, bool GATE>
+__device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const PipeUnit& u, KDA_LDS char* smem,
+                                                 const int tid, const int wave) {
+    using Cfg = PipeCfg<NCW>;
+    using OpT = __bf16;
+    using TIn = __bf16;
+    using QI = Quad<TIn>;
+    using QO = Quad<OpT>;
+    constexpr int DK = Cfg::DK, C = Cfg::C, NT = Cfg::NT, NQ = Cfg::NQ;
+    constexpr int TPS = Cfg::TPS, G = Cfg::G, GPT = Cfg::GPT, SPT = Cfg::SPT;
+    constexpr int PK = Cfg::PK, PT = Cfg::PT, PV = Cfg::PV, PD = Cfg::PD, PDB = Cfg::PDB, NVV = Cfg::NVV;
+    constexpr int NSEG = Cfg::NSEG, VROWS = Cfg::VROWS;
+    constexpr int NKB = DK / 32;
+    constexpr int eLk = (int)((Cfg::oLk - Cfg::oLq) / 2);
+    constexpr int eKd = (int)((Cfg::oKd - Cfg::oLq) / 2);
+    constexpr int eKt = (int)((Cfg::oKt - Cfg::oQt) / 2);
+    constexpr int eBw = (int)((Cfg::oB - Cfg::oTA) / 2);
+
+    KDA_LDS OpT* sQt = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oQt);
+    KDA_LDS OpT* sKpT = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oKpT);
+    KDA_LDS OpT* sTA = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oTA);
+    KDA_LDS TIn* sV = reinterpret_cast<KDA_LDS TIn*>(smem + Cfg::oV);
+    KDA_LDS float* sBeta = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oBeta);
+    KDA_LDS float* sGam = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oGam);
+    KDA_LDS OpT* sLq = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oLq);
+    KDA_LDS float* sTot = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oTot);
+    KDA_LDS float* sD = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oD);
+    KDA_LDS float* sAd = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oAd);
+
+    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int cq = tid % NQ, sg = tid / NQ;   // channel quad, token segment
+    const int ch0 = 4 * cq;
+    KDA_LDS OpT* const pA = lds_pin(sLq + sg * TPS * PK + ch0);         // rows of Lq, Lk, Kd
+    KDA_LDS OpT* const pQK = lds_pin(sQt + sg * TPS * PK + ch0);        // rows of Q~, K~
+    KDA_LDS OpT* const pKp = lds_pin(sKpT + ch0 * PT + sg * TPS);       // K'^T entries
+    KDA_LDS float* const pTotW = lds_pin(sTot + sg * GPT * DK + ch0);
+    KDA_LDS float* const pTotR = lds_pin(sTot + ch0);
+    KDA_LDS float* const pDch = lds_pin(sD + ch0);
+    KDA_LDS OpT* const pK = lds_pin(sLq + lr * PK + 4 * lg);            // fragment rows (tile pairs)
+    KDA_LDS float* const pG = lds_pin(sD + 4 * lg);                     // D table by accumulator row
+    KDA_LDS float* const pBe = lds_pin(sBeta + 4 * lg);                 // beta by accumulator row
+    KDA_LDS OpT* const pW = lds_pin(sTA + 4 * lg * PT + lr);            // accumulator element of TA, B
+    KDA_LDS float* const pAd = lds_pin(sAd + 4 * lg * PD + lr);         // diagonal block, row-major
+    const int wi = wave & (NT - 1);                                     // diagonal block (waves < NT)
+    KDA_LDS float* const pAi = lds_pin(sAd + wi * PDB + (lane & 15) * PD);
+    KDA_LDS OpT* const pTi = lds_pin(sTA + 16 * wi * (PT + 1) + (lane & 15) * PT + (lane >> 4));
+    const int v_row = tid / 16, v_off = (tid % 16) * 8;                 // value rows: 16 vectors each
+    KDA_LDS TIn* const pVc = lds_pin(sV + v_row * PV + v_off);
+
+    const long long HD = u.HD, t_end = u.t_end;
+    const TIn* gq = reinterpret_cast<const TIn*>(a.q) + u.base_tok;
+    const TIn* gk = reinterpret_cast<const TIn*>(a.k) + u.base_tok;
+    constexpr int LAE = GATE ? 2 : 4;                          // bytes per decay-input element
+    const char* gla = GATE ? reinterpret_cast<const char*>(a.gate) + u.base_tok * 2
+                           : reinterpret_cast<const char*>(a.log_alpha + u.base_tok);
+    const long long HDL = HD * LAE;
+    const TIn* gv = reinterpret_cast<const TIn*>(a.v) + u.base_tok;
+    const float* gbeta = a.beta + (long long)u.b * a.T * a.H + u.h;
+    const uint32_t HD2 = (uint32_t)(HD * 2), HDL32 = (uint32_t)HDL;   // token strides in bytes
+
+    // Prefetch of a chunk into registers.  Every address is a uniform row base plus a 32-bit lane
+    // offset; rows past the end of the unit re-read its last row (in bounds).  Such rows need no
+    // zeroing: their decay, beta and value are zeroed where they are consumed, so their U rows are
+    // exactly zero and they add nothing to the state or to earlier outputs.
+    using LaRaw = std::conditional_t<GATE, u32x2_t, f32x4_t>;
+    typename QI::raw pq[TPS], pk[TPS];
+    LaRaw pla[TPS];
+    u32x4_t pv[NVV];
+    float pbeta = 0.0f;
+    auto last_row = [&](long long c0) { return (int)(t_end - 1 - c0 < C - 1 ? t_end - 1 - c0 : C - 1); };
+    auto load_la = [&](long long c0) {
+        const int last = last_row(c0);
+        const char* bl = gla + c0 * HDL;
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) {
+            const uint32_t r = (uint32_t)min(sg * TPS + i, last);
+            pla[i] = *reinterpret_cast<const LaRaw*>(at_byte(bl, pinned_u(r * HDL32 + (uint32_t)(ch0 * LAE))));
+        }
+    };
+    auto load_q = [&](long long c0) {
+        const int last = last_row(c0);
+        const TIn* bq = gq + c0 * HD;
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) {
+            const uint32_t r = (uint32_t)min(sg * TPS + i, last);
+            pq[i] = QI::load(at_byte(bq, pinned_u(r * HD2 + (uint32_t)(ch0 * 2))));
+        }
+    };
+    auto load_k = [&](long long c0) {
+        const int last = last_row(c0);
+        const TIn* bk = gk + c0 * HD;
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) {
+            const uint32_t r = (uint32_t)min(sg * TPS + i, last);
+            pk[i] = QI::load(at_byte(bk, pinned_u(r * HD2 + (uint32_t)(ch0 * 2))));
+        }
+    };
+    auto load_vb = [&](long long c0) {
+        const int last = last_row(c0);
+        pbeta = *at_byte(gbeta + c0 * a.H, pinned_u((uint32_t)min(tid % C, last) * (uint32_t)(a.H * 4)));
+        const TIn* bv = gv + c0 * HD;
+#pragma unroll
+        for (int m = 0; m < NVV; ++m) {
+            const uint32_t r = (uint32_t)min(v_row + VROWS * m, last);
+            pv[m] = *reinterpret_cast<const u32x4_t*>(at_byte(bv, pinned_u(r * HD2 + (uint32_t)(v_off * 2))));
+        }
+    };
+    // next chunk's inputs due for request at the end of interval iv
+    auto prefetch = [&](int iv, int c, long long c0) {
+        if (c + 1 >= u.nchunks) return;
+        if (iv == Cfg::LD_LA) load_la(c0 + C);
+        if (iv == Cfg::LD_Q) load_q(c0 + C);
+        if (iv == Cfg::LD_K) load_k(c0 + C);
+        if (iv == Cfg::LD_VB) load_vb(c0 + C);
+    };
+
+    const int nchunks = u.nchunks;
+    if (nchunks > 0) {
+        load_la(u.t_begin);
+        load_q(u.t_begin);
+        load_k(u.t_begin);
+        load_vb(u.t_begin);
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        const long long c0 = u.t_begin + (long long)c * C;
+        barrier_lds();
+
+        // ---- interval 1, A: log2-decay summed inside decay groups of G tokens; totals to LDS.
+        //      The decay input is pinned here so that this work stays behind the barrier: the
+        //      wait for its loads must not hold the barrier back. ----
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) reg_pin(pla[i]);
+        float g[TPS][4];
+        {
+            const int lastr = last_row(c0);
+            bool okt[TPS];
+#pragma unroll
+            for (int i = 0; i < TPS; ++i) okt[i] = sg * TPS + i <= lastr;
+            float run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < TPS; ++i) {
+                f32x4_t l4;
+                if constexpr (GATE) {
+                    // log alpha = -5 sigmoid(x) = -5 / (1 + 2^{-x log2 e})
+                    const u32x2_t xr = pla[i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t w = e < 2 ? xr[0] : xr[1];
+                        const float x = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+                        l4[e] = kLogAlphaMin * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
+                    }
+                } else {
+                    l4 = pla[i];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float l2 = okt[i] ? fminf(fmaxf(l4[e], kLogAlphaMin), 0.0f) * kLog2e : 0.0f;
+                    run[e] = (i % G == 0) ? l2 : run[e] + l2;
+                    g[i][e] = run[e];
+                }
+                if (i % G == G - 1)
+                    *reinterpret_cast<KDA_LDS f32x4_t*>(pTotW + (i / G) * DK) = f32x4_t{run[0], run[1], run[2], run[3]};
+            }
+        }
+        prefetch(1, c, c0);
+        barrier_lds();
+
+        // ---- interval 2, A': references and decay-scaled operands (same summation order as the
+        //      single-role kernel: group totals in order inside a tile, tile totals in order) ----
+        typename QO::raw qtr[TPS], ktr[TPS];   // Q~, K~ of own rows
+        uint32_t kp[4][TPS / 2];               // K' of own channels, bf16 pairs of tokens
+        f32x4_t gam4;                          // 2^{g_C} of own channels
+        {
+            // hand over v and beta of this chunk first (the state waves read the previous chunk's
+            // in interval 1), freeing their registers
+#pragma unroll
+            for (int m = 0; m < NVV; ++m) {
+                const bool ok = c0 + v_row + VROWS * m < t_end;
+                const u32x4_t x = pv[m];
+                *reinterpret_cast<KDA_LDS u32x4_t*>(pVc + VROWS * m * PV) =
+                    u32x4_t{ok ? x[0] : 0u, ok ? x[1] : 0u, ok ? x[2] : 0u, ok ? x[3] : 0u};
+            }
+            if (tid < C) sBeta[tid] = (c0 + tid < t_end) ? pbeta : 0.0f;
+
+            f32x4_t Rt[NT + 1];
+            Rt[0] = zero4();
+#pragma unroll
+            for (int a2 = 0; a2 < NT; ++a2) {
+                f32x4_t tt = *reinterpret_cast<const KDA_LDS f32x4_t*>(pTotR + a2 * SPT * DK);
+#pragma unroll
+                for (int j = 1; j < SPT; ++j) tt = tt + *reinterpret_cast<const KDA_LDS f32x4_t*>(pTotR + (a2 * SPT + j) * DK);
+                Rt[a2 + 1] = Rt[a2] + tt;
+            }
+            const int at = (sg * TPS) / 16;
+            const int jg0 = (sg * GPT) % SPT;
+            f32x4_t gp[GPT];
+            {
+                const KDA_LDS float* tb = pTotR + at * SPT * DK;
+                f32x4_t run = zero4();
+#pragma unroll
+                for (int j = 0; j < SPT; ++j) {
+#pragma unroll
+                    for (int m = 0; m < GPT; ++m)
+                        if (j == jg0 + m) gp[m] = run;
+                    if (j + 1 < SPT) run = run + *reinterpret_cast<const KDA_LDS f32x4_t*>(tb + j * DK);
+                }
+            }
+            f32x4_t rho = Rt[0], nx = Rt[1];
+#pragma unroll
+            for (int a2 = 1; a2 < NT; ++a2)
+                if (at == a2) {
+                    rho = Rt[a2];
+                    nx = Rt[a2 + 1];
+                }
+            const f32x4_t gC = Rt[NT];
+            float fd[4], fc[4], er[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                fd[e] = fast_exp2(nx[e] - rho[e]);   // 2^{rho_{a+1} - rho_a}
+                fc[e] = fast_exp2(gC[e] - nx[e]);    // 2^{g_C - rho_{a+1}}
+                er[e] = fast_exp2(rho[e]);           // 2^{rho_a}
+                gam4[e] = fast_exp2(gC[e]);
+            }
+            // table 2^{rho_{a+1} - rho_a}: row a formed by the first segment of tile a
+            if (sg % (NSEG / NT) == 0) {
+                const int ta = sg / (NSEG / NT);
+                f32x4_t r0 = Rt[0], r1 = Rt[1];
+#pragma unroll
+                for (int a2 = 1; a2 < NT; ++a2)
+                    if (ta == a2) {
+                        r0 = Rt[a2];
+                        r1 = Rt[a2 + 1];
+                    }
+                f32x4_t d4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d4[e] = fast_exp2(r1[e] - r0[e]);
+                *reinterpret_cast<KDA_LDS f32x4_t*>(pDch + ta * DK) = d4;
+            }
+#pragma unroll
+            for (int i = 0; i < TPS; ++i) {
+                float lq[4], lk[4], kd[4], qt[4], kt[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float loc = gp[i / G][e] + g[i][e];   // g - rho_a, in [-115.4, 0]
+                    const float x = fast_exp2(loc);
+                    const float y = fast_exp2(-loc);
+                    const float kv = QI::get(pk[i], e);
+                    const float qv = QI::get(pq[i], e);
+                    const float xe = x * er[e];
+                    lq[e] = qv * x;
+                    qt[e] = qv * xe;
+                    lk[e] = kv * x;
+                    kt[e] = kv * xe;
+                    kd[e] = kv * y;
+                    const float kpv = (kd[e] * fd[e]) * fc[e];
+                    if (i & 1) kp[e][i / 2] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)kpv) << 16;
+                    else kp[e][i / 2] = __builtin_bit_cast(uint16_t, (__bf16)kpv);
+                }
+                QO::store(pA + i * PK, lq[0], lq[1], lq[2], lq[3]);
+                QO::store(pA + eLk + i * PK, lk[0], lk[1], lk[2], lk[3]);
+                QO::store(pA + eKd + i * PK, kd[0], kd[1], kd[2], kd[3]);
+                qtr[i] = QO::pack(qt[0], qt[1], qt[2], qt[3]);
+                ktr[i] = QO::pack(kt[0], kt[1], kt[2], kt[3]);
+            }
+        }
+        prefetch(2, c, c0);
+        barrier_lds();
+
+        // ---- interval 3: hand over K~ and Q~ (the state waves read the previous chunk's in
+        //      intervals 1 and 2), then B: decay-weighted KK^T and QK^T tiles, one dense product
+        //      per tile pair ----
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) {
+            QO::store_raw(pQK + i * PK, qtr[i]);
+            QO::store_raw(pQK + eKt + i * PK, ktr[i]);
+        }
+        {
+            constexpr int NP = NT * (NT + 1) / 2;
+            static_for<0, NP>([&](auto PIc) {
+                constexpr int pi = decltype(PIc)::value;
+                constexpr int ar = pair_row(pi);
+                constexpr int ac = pi - ar * (ar + 1) / 2;
+                if (pipe_pair_owner<NCW>(pi) != wave) return;   // wave-uniform
+                f32x4_t accA = zero4(), accB = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    Frag<OpT> fk, fq, fr;
+                    frag_ld(fk, pK + eLk + 16 * ar * PK + 32 * kb);
+                    frag_ld(fq, pK + 16 * ar * PK + 32 * kb);
+                    frag_ld(fr, pK + eKd + 16 * ac * PK + 32 * kb);
+                    if constexpr (ac < ar) {
+                        // R = Kd 2^{rho_ar - rho_ac}, one tile step at a time
+                        float val[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) val[j] = fr.get(j);
+#pragma unroll
+                        for (int m = ac; m < ar; ++m) {
+                            float d8[8];
+                            f32x8_ld(d8, pG + m * DK + 32 * kb);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) val[j] *= d8[j];
+                        }
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) fr.set(j, val[j]);
+                    }
+                    accA = mma(fk, fr, accA);
+                    accB = mma(fq, fr, accB);
+                }
+                const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pBe + 16 * ar);
+                if constexpr (ac == ar) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int rl = 4 * lg + j;
+                        pAd[ar * PDB + j * PD] = (lr < rl) ? accA[j] * bt4[j] : 0.0f;
+                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pW[16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(-accA[j] * bt4[j]);
+                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(accB[j]);
+                    }
+                }
+            });
+        }
+        prefetch(3, c, c0);
+        barrier_lds();
+
+        // ---- interval 4: diagonal blocks T_aa = (I + A_aa)^{-1}, wave a inverting block a by
+        //      forward substitution with the pivot row broadcast inside 16-lane rows (DPP) ----
+        if (wave < NT) {
+            const int p = lane & 15, cgp = lane >> 4;
+            float na[16];   // -A_aa[p][i]
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4_t v4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pAi + 4 * q4);
+                na[4 * q4] = -v4[0]; na[4 * q4 + 1] = -v4[1]; na[4 * q4 + 2] = -v4[2]; na[4 * q4 + 3] = -v4[3];
+            }
+            float t[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) t[r] = (p == cgp + 4 * r) ? 1.0f : 0.0f;
+            static_for<0, 15>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) t[r] = fmaf(na[i], row_bcast<i>(t[r]), t[r]);
+            });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pTi[4 * r] = from_f32<OpT>(t[r]);
+        }
+        // hand over K'^T and 2^{g_C} (the state waves read the previous chunk's in interval 3)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (TPS == 8)
+                *reinterpret_cast<KDA_LDS u32x4_t*>(pKp + e * PT) = u32x4_t{kp[e][0], kp[e][1], kp[e][2], kp[e][3]};
+            else
+                *reinterpret_cast<KDA_LDS u32x2_t*>(pKp + e * PT) = u32x2_t{kp[e][0], kp[e][1]};
+        }
+        if (sg == 0) *reinterpret_cast<KDA_LDS f32x4_t*>(sGam + ch0) = gam4;
+        prefetch(4, c, c0);
+    }
+    // the state waves run the last chunk
+#pragma unroll
+    for (int i = 0; i < 4; ++i) barrier_lds();
+}
+
+// State waves (NCW .. NCW+3): state wave sw holds state columns 32 sw .. 32 sw + 31 in
+// fp32 registers and runs the state-dependent products of each chunk.  Four barriers while the
+// chunk waves prepare the first chunk, then four per chunk.
+template <int NCW>
+__device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const PipeUnit& u, KDA_LDS char* smem,
+                                                 const int tid, const int sw) {
+    using Cfg = PipeCfg<NCW>;
+    using OpT = __bf16;
+    using TIn = __bf16;
+    constexpr int DK = Cfg::DK, C = Cfg::C, NT = Cfg::NT, NTB = Cfg::NTB, NCT = Cfg::NCT;
+    constexpr int PK = Cfg::PK, PT = Cfg::PT, PV = Cfg::PV;
+    constexpr int NIT = DK / 16, NKB = DK / 32;
+    constexpr int eKt = (int)((Cfg::oKt - Cfg::oQt) / 2);
+    constexpr int eTA = (int)((Cfg::oTA - Cfg::oKpT) / 2);
+    constexpr int eB = (int)((Cfg::oB - Cfg::oKpT) / 2);
+
+    KDA_LDS OpT* sQt = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oQt);
+    KDA_LDS OpT* sKpT = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oKpT);
+    KDA_LDS TIn* sV = reinterpret_cast<KDA_LDS TIn*>(smem + Cfg::oV);
+    KDA_LDS float* sBeta = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oBeta);
+    KDA_LDS float* sGam = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oGam);
+
+    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int colw = 32 * sw;   // first state column of this wave
+
+    // lane holds S[16 it + 4 lg + j][colw + 16 ct + lr]; its byte offset in a DK x DK state, formed
+    // where it is used (kept opaque so that no 64-bit addresses are held across the chunk loop)
+    auto st_off = [&](int it, int ct, int j) {
+        return pinned_u((uint32_t)(((16 * it + 4 * lg + j) * DK + colw + 16 * ct + lr) * 4));
+    };
+    f32x4_t st[NIT][NCT];
+    if (a.init_mode == 1) {
+        const float* sin = a.s_in + (long long)u.bh * a.sin_bh_stride + (long long)u.s * a.sin_seg_stride;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    st[it][ct][j] = *at_byte(sin, st_off(it, ct, j));
+    } else {
+        const bool ident = a.init_mode == 2;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    st[it][ct][j] = (ident && 16 * it + 4 * lg + j == colw + 16 * ct + lr) ? 1.0f : 0.0f;
+    }
+
+    KDA_LDS OpT* const pQs = lds_pin(sQt + lr * PK + 4 * lg);             // fragment rows of Q~, K~
+    KDA_LDS OpT* const pTs = lds_pin(sKpT + lr * PT + 4 * lg);            // fragment rows of K'^T, TA, B
+    KDA_LDS TIn* const pVs = lds_pin(sV + 4 * lg * PV + colw + lr);       // value in accumulator layout
+    KDA_LDS float* const pBs = lds_pin(sBeta + 4 * lg);
+    KDA_LDS float* const pGs = lds_pin(sGam + 4 * lg);
+    TIn* const go = a.o ? reinterpret_cast<TIn*>(a.o) + u.base_tok : nullptr;
+    // outputs are formed transposed (O^T = S^T Q~^T + U^T Bqk^T: the same fragments with the
+    // operands swapped), so a lane holds 4 adjacent outputs of one token: token lr of the tile,
+    // columns colw + 16 ct + 4 lg .. + 3, stored with one 8-byte store
+    const uint32_t boO = (uint32_t)((lr * u.HD + colw + 4 * lg) * 2);
+    const long long HD = u.HD, t_end = u.t_end;
+
+    // S as an operand, one 32-row block at a time: B operand of K~ S and Q~ S, or equally the A
+    // operand of S^T Q~^T (the fragment layout is the same for both roles)
+    auto s_frag = [&](Frag<OpT> (&fs)[NCT], int kb) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc_pair_frag(fs[ct], st[2 * kb][ct], st[2 * kb + 1][ct], true);
+    };
+    // X = K~ S and RHS = beta (V - X) of a chunk, from the state before it
+    f32x4_t Rh[NT][NCT];
+    auto x_rhs = [&]() {
+#pragma unroll
+        for (int ar = 0; ar < NT; ++ar)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            Frag<OpT> fs[NCT];
+            s_frag(fs, kb);
+#pragma unroll
+            for (int ar = 0; ar < NT; ++ar) {
+                Frag<OpT> fk;
+                frag_ld(fk, pQs + eKt + 16 * ar * PK + 32 * kb);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = mma(fk, fs[ct], Rh[ar][ct]);
+            }
+        }
+#pragma unroll
+        for (int ar = 0; ar < NT; ++ar) {
+            const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pBs + 16 * ar);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    Rh[ar][ct][j] = bt4[j] * (to_f32<TIn>(pVs[(16 * ar + j) * PV + 16 * ct]) - Rh[ar][ct][j]);
+        }
+    };
+
+    // the chunk waves prepare the first chunk; its X and RHS run beside their diagonal inverses
+#pragma unroll
+    for (int i = 0; i < 4; ++i) barrier_lds();
+    if (u.nchunks > 0) x_rhs();
+
+    for (int c = 0; c < u.nchunks; ++c) {
+        const long long c0 = u.t_begin + (long long)c * C;
+        barrier_lds();
+
+        // ---- interval 1: U_a = T_aa (RHS_a - sum_{b<a} A_ab U_b) ----
+        f32x4_t U[NT][NCT];
+        Frag<OpT> fU[NTB][NCT];
+#pragma unroll
+        for (int ar = 0; ar < NT; ++ar) {
+            f32x4_t W[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) W[ct] = Rh[ar][ct];
+#pragma unroll
+            for (int kb = 0; kb < ar / 2; ++kb) {
+                Frag<OpT> fa;
+                frag_ld(fa, pTs + eTA + 16 * ar * PT + 32 * kb);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) W[ct] = mma(fa, fU[kb][ct], W[ct]);
+            }
+            if (ar & 1) {
+                Frag<OpT> fa;
+                frag_ld_lo(fa, pTs + eTA + 16 * ar * PT + 16 * (ar - 1));
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    Frag<OpT> fb;
+                    acc_pair_frag(fb, U[ar - 1][ct], U[ar - 1][ct], false);
+                    W[ct] = mma(fa, fb, W[ct]);
+                }
+            }
+            Frag<OpT> ft;
+            frag_ld_lo(ft, pTs + eTA + 16 * ar * PT + 16 * ar);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                Frag<OpT> fw;
+                acc_pair_frag(fw, W[ct], W[ct], false);
+                U[ar][ct] = mma(ft, fw, zero4());
+            }
+            if (ar & 1) {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) acc_pair_frag(fU[ar / 2][ct], U[ar - 1][ct], U[ar][ct], true);
+            }
+        }
+        barrier_lds();
+
+        // ---- interval 2: O^T = S^T Q~^T + U^T Bqk^T, stored from the accumulators ----
+        if (go) {
+            f32x4_t Oa[NT][NCT];
+#pragma unroll
+            for (int ar = 0; ar < NT; ++ar)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) Oa[ar][ct] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                Frag<OpT> fs[NCT];
+                s_frag(fs, kb);
+#pragma unroll
+                for (int ar = 0; ar < NT; ++ar) {
+                    Frag<OpT> fq;
+                    frag_ld(fq, pQs + 16 * ar * PK + 32 * kb);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) Oa[ar][ct] = mma(fs[ct], fq, Oa[ar][ct]);
+                }
+            }
+#pragma unroll
+            for (int ar = 0; ar < NT; ++ar) {
+                f32x4_t O[NCT];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) O[ct] = Oa[ar][ct];
+#pragma unroll
+                for (int kb = 0; kb <= ar / 2; ++kb) {
+                    Frag<OpT> fb;
+                    frag_ld(fb, pTs + eB + 16 * ar * PT + 32 * kb);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) O[ct] = mma(fU[kb][ct], fb, O[ct]);
+                }
+                if (c0 + 16 * ar + lr < t_end) {
+                    TIn* const orow = go + (c0 + 16 * ar) * HD;
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+                        *reinterpret_cast<u32x2_t*>(at_byte(orow, pinned_u(boO + 32 * ct))) =
+                            Quad<TIn>::pack(O[ct][0], O[ct][1], O[ct][2], O[ct][3]);
+                }
+            }
+        }
+        barrier_lds();
+
+        // ---- interval 3: S <- Diag(2^{g_C}) S + K'^T U ----
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const f32x4_t gm = *reinterpret_cast<const KDA_LDS f32x4_t*>(pGs + 16 * it);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st[it][ct][j] *= gm[j];
+#pragma unroll
+            for (int kb = 0; kb < NTB; ++kb) {
+                Frag<OpT> fkp;
+                frag_ld(fkp, pTs + 16 * it * PT + 32 * kb);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) st[it][ct] = mma(fkp, fU[kb][ct], st[it][ct]);
+            }
+        }
+        if (a.s_ckpt) {   // the state after a full chunk ending on a multiple of ckpt_every
+            const long long pend = c0 + C;
+            if (pend <= t_end && pend % a.ckpt_every == 0) {
+                const long long ci = pend / a.ckpt_every - 1;
+                float* sc = a.s_ckpt + (((long long)u.b * a.n_ckpt + ci) * a.H + u.h) * (long long)(DK * DK);
+#pragma unroll
+                for (int it = 0; it < NIT; ++it)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            *at_byte(sc, st_off(it, ct, j)) = st[it][ct][j];
+            }
+        }
+        barrier_lds();
+
+        // ---- interval 4: X and RHS of the next chunk (the chunk waves handed over its K~, V and
+        //      beta in intervals 2 and 3 and invert its diagonal blocks meanwhile) ----
+        if (c + 1 < u.nchunks) x_rhs();
+    }
+
+    if (a.s_out && (a.out_seg < 0 || a.out_seg == u.s)) {
+        float* so = a.s_out + (long long)u.bh * a.sout_bh_stride + (long long)u.s * a.sout_seg_stride;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *at_byte(so, st_off(it, ct, j)) = st[it][ct][j];
+    }
+}
+
+// One workgroup per unit (sequence, head, segment), all 128 state columns.  The two roles run
+// separate loops with the same number of workgroup barriers (4 per chunk plus 4), so every
+// barrier is met by all eight waves; the registers of each role are allocated on its own.
+template <int NCW, bool GATE>
+__global__ __launch_bounds__(64 * (NCW + 4)) void kda_prefill_pipe_kernel(const PrefillArgs a) {
+    using Cfg = PipeCfg<NCW>;
+    constexpr int C = Cfg::C, PT = Cfg::PT, DK = Cfg::DK, NTH = Cfg::NTH;
+    __shared__ __align__(16) char smem_[Cfg::LDS];
+    KDA_LDS char* smem = (KDA_LDS char*)smem_;
+
+    const int bid = blockIdx.x;
+    const int unit = (bid >> 3) * 8 + (bid & 7);
+    if (unit >= a.n_units) return;
+    PipeUnit u;
+    const int sl = unit % a.n_seg_launch;
+    u.bh = unit / a.n_seg_launch;
+    u.h = u.bh % a.H;
+    u.b = u.bh / a.H;
+    u.s = a.seg0 + sl;
+    u.t_begin = (long long)u.s * a.seg_len;
+    u.t_end = (u.t_begin + a.seg_len < a.T) ? u.t_begin + a.seg_len : a.T;
+    const long long ntok = u.t_end - u.t_begin;
+    u.nchunks = ntok > 0 ? (int)((ntok + C - 1) / C) : 0;
+    u.HD = (long long)a.H * DK;
+    u.base_tok = (long long)u.b * a.T * u.HD + (long long)u.h * DK;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // zero the token-padded operand arrays once (parts never written stay zero)
+    {
+        KDA_LDS __bf16* sKpT = reinterpret_cast<KDA_LDS __bf16*>(smem + Cfg::oKpT);
+        KDA_LDS __bf16* sTA = reinterpret_cast<KDA_LDS __bf16*>(smem + Cfg::oTA);
+        KDA_LDS __bf16* sB = reinterpret_cast<KDA_LDS __bf16*>(smem + Cfg::oB);
+        for (int e = tid; e < C * PT; e += NTH) {
+            sTA[e] = from_f32<__bf16>(0.0f);
+            sB[e] = from_f32<__bf16>(0.0f);
+        }
+        for (int e = tid; e < DK * PT; e += NTH) sKpT[e] = from_f32<__bf16>(0.0f);
+    }
+    if (wave < NCW) pipe_chunk_waves<NCW, GATE>(a, u, smem, tid, wave);
+    else pipe_state_waves<NCW>(a, u, smem, tid, wave - NCW);
+}
+
+template <int NCW, bool GATE>
+hipError_t launch_prefill_pipe(const PrefillArgs& a, hipStream_t stream) {
+    if (a.n_vs != 1 || a.lens || a.zero_values || (a.gate != nullptr) != GATE) return hipErrorInvalidValue;
+    const long long nblk = ((long long)a.n_units + 7) / 8 * 8;
+    if (nblk <= 0) return hipSuccess;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((kda_prefill_pipe_kernel<NCW, GATE>), dim3((unsigned)nblk), dim3(64 * (NCW + 4)), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace kda
