@@ -92,6 +92,14 @@ __device__ __forceinline__ void frag_ld(Frag<float>& f, const KDA_LDS float* p) 
     f.v[4] = hi[0]; f.v[5] = hi[1]; f.v[6] = hi[2]; f.v[7] = hi[3];
 }
 
+// The same eight slots from two separate LDS addresses (slots 0..3 at lo, 4..7 at hi): rows whose
+// 4-element groups are stored permuted.
+__device__ __forceinline__ void frag_ld2(Frag<__bf16>& f, const KDA_LDS __bf16* lo, const KDA_LDS __bf16* hi) {
+    const bf16x4_t a = *reinterpret_cast<const KDA_LDS bf16x4_t*>(lo);
+    const bf16x4_t b = *reinterpret_cast<const KDA_LDS bf16x4_t*>(hi);
+    f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Only the lower four slots from LDS, the upper four zero: a 16-wide contraction block.
 __device__ __forceinline__ void frag_ld_lo(Frag<__bf16>& f, const KDA_LDS __bf16* p) {
     const bf16x4_t lo = *reinterpret_cast<const KDA_LDS bf16x4_t*>(p);
@@ -186,7 +194,7 @@ template <typename T> __device__ __forceinline__ KDA_LDS T* lds_pin(KDA_LDS T* p
 // Value of x in lane I of this lane's 16-lane row (DPP row broadcast).
 template <int I> __device__ __forceinline__ float row_bcast(float x) {
     static_assert(I >= 0 && I < 16, "row lane");
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + I, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + I, 0xF, 0xF, true));
 }
 // Marks a register value as redefined at this point: computation that reads it cannot be moved
 // above here (a load into it is waited for here, not earlier).

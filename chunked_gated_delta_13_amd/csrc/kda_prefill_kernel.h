@@ -626,7 +626,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
             static_for<0, 15>([&](auto I) {
                 constexpr int i = decltype(I)::value;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) t[r] = fmaf(na[i], row_bcast<i>(t[r]), t[r]);
+                for (int r = 0; r < 4; ++r) t[r] = fmaf(row_bcast<i>(t[r]), na[i], t[r]);
             });
 #pragma unroll
             for (int r = 0; r < 4; ++r) pTi[4 * r] = from_f32<OpT>(t[r]);

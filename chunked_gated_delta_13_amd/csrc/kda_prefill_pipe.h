@@ -140,7 +140,12 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
     const int ch0 = 4 * cq;
     KDA_LDS OpT* const pA = lds_pin(sLq + sg * TPS * PK + ch0);         // rows of Lq, Lk, Kd
     KDA_LDS OpT* const pQK = lds_pin(sQt + sg * TPS * PK + ch0);        // rows of Q~, K~
-    KDA_LDS OpT* const pKp = lds_pin(sKpT + ch0 * PT + sg * TPS);       // K'^T entries
+    // K'^T rows hold their 4-token groups permuted by row, column c at c ^ 4 ((row >> 3) & 15):
+    // the transposed stores below then hit distinct LDS banks (the plain layout serialises them
+    // about 4-fold), and the state waves' fragment loads stay conflict-free
+    const int kswz = 4 * ((cq >> 1) & 15);                              // ((ch0 + e) >> 3) == cq >> 1
+    KDA_LDS OpT* const pKp0 = lds_pin(sKpT + ch0 * PT + ((sg * TPS) ^ kswz));
+    KDA_LDS OpT* const pKp1 = lds_pin(sKpT + ch0 * PT + ((sg * TPS + 4) ^ kswz));   // TPS == 8
     KDA_LDS float* const pTotW = lds_pin(sTot + sg * GPT * DK + ch0);
     KDA_LDS float* const pTotR = lds_pin(sTot + ch0);
     KDA_LDS float* const pDch = lds_pin(sD + ch0);
@@ -450,7 +455,7 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
             static_for<0, 15>([&](auto I) {
                 constexpr int i = decltype(I)::value;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) t[r] = fmaf(na[i], row_bcast<i>(t[r]), t[r]);
+                for (int r = 0; r < 4; ++r) t[r] = fmaf(row_bcast<i>(t[r]), na[i], t[r]);
             });
 #pragma unroll
             for (int r = 0; r < 4; ++r) pTi[4 * r] = from_f32<OpT>(t[r]);
@@ -458,10 +463,9 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
         // hand over K'^T and 2^{g_C} (the state waves read the previous chunk's in interval 3)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+            *reinterpret_cast<KDA_LDS u32x2_t*>(pKp0 + e * PT) = u32x2_t{kp[e][0], kp[e][1]};
             if constexpr (TPS == 8)
-                *reinterpret_cast<KDA_LDS u32x4_t*>(pKp + e * PT) = u32x4_t{kp[e][0], kp[e][1], kp[e][2], kp[e][3]};
-            else
-                *reinterpret_cast<KDA_LDS u32x2_t*>(pKp + e * PT) = u32x2_t{kp[e][0], kp[e][1]};
+                *reinterpret_cast<KDA_LDS u32x2_t*>(pKp1 + e * PT) = u32x2_t{kp[e][2], kp[e][3]};
         }
         if (sg == 0) *reinterpret_cast<KDA_LDS f32x4_t*>(sGam + ch0) = gam4;
         prefetch(4, c, c0);
@@ -523,7 +527,12 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
     }
 
     KDA_LDS OpT* const pQs = lds_pin(sQt + lr * PK + 4 * lg);             // fragment rows of Q~, K~
-    KDA_LDS OpT* const pTs = lds_pin(sKpT + lr * PT + 4 * lg);            // fragment rows of K'^T, TA, B
+    KDA_LDS OpT* const pTs = lds_pin(sKpT + lr * PT + 4 * lg);            // fragment rows of TA, B
+    // fragment rows of the permuted K'^T (row 16 it + lr holds column c at c ^ (8 it + 4 (lr >> 3))):
+    // one base for even and one for odd it, the rest of the permutation is an immediate offset
+    const int hsw = lr >> 3;
+    KDA_LDS OpT* const pKs0 = lds_pin(sKpT + lr * PT + 4 * (lg ^ hsw));
+    KDA_LDS OpT* const pKs1 = lds_pin(sKpT + lr * PT + ((4 * (lg ^ hsw)) ^ 8));
     KDA_LDS TIn* const pVs = lds_pin(sV + 4 * lg * PV + colw + lr);       // value in accumulator layout
     KDA_LDS float* const pBs = lds_pin(sBeta + 4 * lg);
     KDA_LDS float* const pGs = lds_pin(sGam + 4 * lg);
@@ -672,7 +681,9 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
 #pragma unroll
             for (int kb = 0; kb < NTB; ++kb) {
                 Frag<OpT> fkp;
-                frag_ld(fkp, pTs + 16 * it * PT + 32 * kb);
+                const KDA_LDS OpT* const kb0 = ((it & 1) ? pKs1 : pKs0) + 16 * it * PT;
+                const int hi = (8 * it) & 48;
+                frag_ld2(fkp, kb0 + ((32 * kb) ^ hi), kb0 + ((32 * kb + 16) ^ hi));
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) st[it][ct] = mma(fkp, fU[kb][ct], st[it][ct]);
             }
