@@ -5,16 +5,17 @@
 // (decay, decay-scaled operands, tile pairs, diagonal inverses: VALU-heavy) and the
 // state-dependent work (state products: matrix cores and LDS) never overlap.  Here the waves of
 // a workgroup take two roles and two chunks are in flight:
-//   NCW "chunk waves" (4 or 8) prepare chunk c+1: phases A, A', B and the diagonal inverses;
+//   NCW "chunk waves" (4 or 8) prepare chunk c+1: decay sums (A and a prefix pass), decay-scaled
+//   operands (A'), tile pairs (B) and the diagonal inverses;
 //   4 "state waves" hold the fp32 state, 32 columns each, and run chunk c:
 //   X = K~S and RHS (from the state after chunk c-1), U, O, state update.
 // Every SIMD hosts waves of both roles, so VALU work of one role issues while the other waits on
 // the matrix cores or LDS.  Per loop iteration there are four barrier intervals, the same for
 // both roles:
-//   1: A(c+1)          | U(c)
-//   2: A'(c+1)         | O(c)            chunk waves hand over V, beta of c+1
-//   3: B(c+1)          | state update(c) chunk waves hand over K~, Q~ of c+1
-//   4: inverses(c+1)   | X, RHS(c+1)     chunk waves hand over K'^T, 2^{g_C} of c+1
+//   1: prefix(c+1)             | U(c)
+//   2: A'(c+1)                 | O(c)            chunk waves hand over V, beta of c+1
+//   3: B(c+1)                  | state update(c) chunk waves hand over K~, Q~ of c+1
+//   4: inverses(c+1), A(c+2)   | X, RHS(c+1)     chunk waves hand over K'^T, 2^{g_C} of c+1
 // An operand array of chunk c is overwritten for c+1 only in an interval after the last state
 // wave read it, so it needs one copy.  The arithmetic of every phase is that of
 // kda_prefill_kernel.h (same decay summation order, same products); sources as cited there:
@@ -77,7 +78,9 @@ struct PipeCfg {
     static constexpr size_t oKd = oLk + pipe_al(2 * C * PK);
     static constexpr size_t oTot = oKd + pipe_al(2 * C * PK);
     static constexpr size_t oD = oTot + pipe_al(4 * 16 * DK);
-    static constexpr size_t oAd = oD + pipe_al(4 * NT * DK);
+    static constexpr size_t oE = oD + pipe_al(4 * NT * DK);
+    static constexpr size_t oF = oE + pipe_al(4 * (NT + 1) * DK);
+    static constexpr size_t oAd = oF + pipe_al(4 * NT * DK);
     static constexpr size_t LDS = oAd + pipe_al(4 * NT * PDB);
     static_assert(LDS <= 160 * 1024, "LDS budget of one gfx950 workgroup");
     static_assert((NCW == 4 && TPS == 8) || (NCW == 8 && TPS == 4), "segment layout of the chunk waves");
@@ -133,6 +136,8 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
     KDA_LDS OpT* sLq = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oLq);
     KDA_LDS float* sTot = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oTot);
     KDA_LDS float* sD = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oD);
+    KDA_LDS float* sE = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oE);
+    KDA_LDS float* sF = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oF);
     KDA_LDS float* sAd = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oAd);
 
     const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -147,8 +152,6 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
     KDA_LDS OpT* const pKp0 = lds_pin(sKpT + ch0 * PT + ((sg * TPS) ^ kswz));
     KDA_LDS OpT* const pKp1 = lds_pin(sKpT + ch0 * PT + ((sg * TPS + 4) ^ kswz));   // TPS == 8
     KDA_LDS float* const pTotW = lds_pin(sTot + sg * GPT * DK + ch0);
-    KDA_LDS float* const pTotR = lds_pin(sTot + ch0);
-    KDA_LDS float* const pDch = lds_pin(sD + ch0);
     KDA_LDS OpT* const pK = lds_pin(sLq + lr * PK + 4 * lg);            // fragment rows (tile pairs)
     KDA_LDS float* const pG = lds_pin(sD + 4 * lg);                     // D table by accumulator row
     KDA_LDS float* const pBe = lds_pin(sBeta + 4 * lg);                 // beta by accumulator row
@@ -227,65 +230,99 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
         if (iv == Cfg::LD_VB) load_vb(c0 + C);
     };
 
+    // A: log2-decay summed inside decay groups of G tokens (g, kept in registers until A');
+    // group totals to LDS
+    float g[TPS][4];
+    auto phase_a = [&](long long c0) {
+        const int lastr = last_row(c0);
+        bool okt[TPS];
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) okt[i] = sg * TPS + i <= lastr;
+        float run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) {
+            f32x4_t l4;
+            if constexpr (GATE) {
+                // log alpha = -5 sigmoid(x) = -5 / (1 + 2^{-x log2 e})
+                const u32x2_t xr = pla[i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = e < 2 ? xr[0] : xr[1];
+                    const float x = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+                    l4[e] = kLogAlphaMin * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
+                }
+            } else {
+                l4 = pla[i];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float l2 = okt[i] ? fminf(fmaxf(l4[e], kLogAlphaMin), 0.0f) * kLog2e : 0.0f;
+                run[e] = (i % G == 0) ? l2 : run[e] + l2;
+                g[i][e] = run[e];
+            }
+            if (i % G == G - 1)
+                *reinterpret_cast<KDA_LDS f32x4_t*>(pTotW + (i / G) * DK) = f32x4_t{run[0], run[1], run[2], run[3]};
+        }
+    };
+    // Prefix pass, one channel per thread (threads 0..DK-1): from the group totals, in the
+    // canonical order (group totals in order inside a tile, tile totals in order across the
+    // chunk), rho_a for every tile and, in place of each group total, the sum of the groups
+    // before it inside its tile; then the tables 2^{rho_a} (a = 0..NT), 2^{rho_{a+1} - rho_a}
+    // and 2^{g_C - rho_{a+1}}.
+    auto prefix_pass = [&]() {
+        const int ch = tid;
+        float tot[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tot[j] = sTot[j * DK + ch];
+        float Rt[NT + 1];
+        Rt[0] = 0.0f;
+#pragma unroll
+        for (int a2 = 0; a2 < NT; ++a2) {
+            float run = 0.0f;
+#pragma unroll
+            for (int j = 0; j < SPT; ++j) {
+                sTot[(a2 * SPT + j) * DK + ch] = run;
+                if (j + 1 < SPT) run = run + tot[a2 * SPT + j];
+            }
+            float tt = tot[a2 * SPT];
+#pragma unroll
+            for (int j = 1; j < SPT; ++j) tt = tt + tot[a2 * SPT + j];
+            Rt[a2 + 1] = Rt[a2] + tt;
+        }
+#pragma unroll
+        for (int a2 = 0; a2 <= NT; ++a2) sE[a2 * DK + ch] = fast_exp2(Rt[a2]);
+#pragma unroll
+        for (int a2 = 0; a2 < NT; ++a2) {
+            sD[a2 * DK + ch] = fast_exp2(Rt[a2 + 1] - Rt[a2]);
+            sF[a2 * DK + ch] = fast_exp2(Rt[NT] - Rt[a2 + 1]);
+        }
+    };
+    static_assert(16 / G == Cfg::SPT && NT * Cfg::SPT == 16, "16 decay groups per chunk");
+
     const int nchunks = u.nchunks;
     if (nchunks > 0) {
         load_la(u.t_begin);
         load_q(u.t_begin);
         load_k(u.t_begin);
         load_vb(u.t_begin);
+        phase_a(u.t_begin);
     }
     for (int c = 0; c < nchunks; ++c) {
         const long long c0 = u.t_begin + (long long)c * C;
         barrier_lds();
 
-        // ---- interval 1, A: log2-decay summed inside decay groups of G tokens; totals to LDS.
-        //      The decay input is pinned here so that this work stays behind the barrier: the
-        //      wait for its loads must not hold the barrier back. ----
-#pragma unroll
-        for (int i = 0; i < TPS; ++i) reg_pin(pla[i]);
-        float g[TPS][4];
-        {
-            const int lastr = last_row(c0);
-            bool okt[TPS];
-#pragma unroll
-            for (int i = 0; i < TPS; ++i) okt[i] = sg * TPS + i <= lastr;
-            float run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int i = 0; i < TPS; ++i) {
-                f32x4_t l4;
-                if constexpr (GATE) {
-                    // log alpha = -5 sigmoid(x) = -5 / (1 + 2^{-x log2 e})
-                    const u32x2_t xr = pla[i];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t w = e < 2 ? xr[0] : xr[1];
-                        const float x = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-                        l4[e] = kLogAlphaMin * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
-                    }
-                } else {
-                    l4 = pla[i];
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float l2 = okt[i] ? fminf(fmaxf(l4[e], kLogAlphaMin), 0.0f) * kLog2e : 0.0f;
-                    run[e] = (i % G == 0) ? l2 : run[e] + l2;
-                    g[i][e] = run[e];
-                }
-                if (i % G == G - 1)
-                    *reinterpret_cast<KDA_LDS f32x4_t*>(pTotW + (i / G) * DK) = f32x4_t{run[0], run[1], run[2], run[3]};
-            }
-        }
+        // ---- interval 1: prefix pass over this chunk's group totals (written by phase A in the
+        //      previous interval 4, or before the loop) ----
+        if (tid < DK) prefix_pass();
         prefetch(1, c, c0);
         barrier_lds();
 
-        // ---- interval 2, A': references and decay-scaled operands (same summation order as the
-        //      single-role kernel: group totals in order inside a tile, tile totals in order) ----
+        // ---- interval 2, A': decay-scaled operands ----
         typename QO::raw qtr[TPS], ktr[TPS];   // Q~, K~ of own rows
         uint32_t kp[4][TPS / 2];               // K' of own channels, bf16 pairs of tokens
-        f32x4_t gam4;                          // 2^{g_C} of own channels
         {
             // hand over v and beta of this chunk first (the state waves read the previous chunk's
-            // in interval 1), freeing their registers
+            // in interval 4 of the previous iteration), freeing their registers
 #pragma unroll
             for (int m = 0; m < NVV; ++m) {
                 const bool ok = c0 + v_row + VROWS * m < t_end;
@@ -295,59 +332,19 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
             }
             if (tid < C) sBeta[tid] = (c0 + tid < t_end) ? pbeta : 0.0f;
 
-            f32x4_t Rt[NT + 1];
-            Rt[0] = zero4();
+            const int at = (sg * TPS) / 16;    // this segment's row tile
+            f32x4_t gp[GPT];                   // in-tile sums before own groups
 #pragma unroll
-            for (int a2 = 0; a2 < NT; ++a2) {
-                f32x4_t tt = *reinterpret_cast<const KDA_LDS f32x4_t*>(pTotR + a2 * SPT * DK);
-#pragma unroll
-                for (int j = 1; j < SPT; ++j) tt = tt + *reinterpret_cast<const KDA_LDS f32x4_t*>(pTotR + (a2 * SPT + j) * DK);
-                Rt[a2 + 1] = Rt[a2] + tt;
-            }
-            const int at = (sg * TPS) / 16;
-            const int jg0 = (sg * GPT) % SPT;
-            f32x4_t gp[GPT];
-            {
-                const KDA_LDS float* tb = pTotR + at * SPT * DK;
-                f32x4_t run = zero4();
-#pragma unroll
-                for (int j = 0; j < SPT; ++j) {
-#pragma unroll
-                    for (int m = 0; m < GPT; ++m)
-                        if (j == jg0 + m) gp[m] = run;
-                    if (j + 1 < SPT) run = run + *reinterpret_cast<const KDA_LDS f32x4_t*>(tb + j * DK);
-                }
-            }
-            f32x4_t rho = Rt[0], nx = Rt[1];
-#pragma unroll
-            for (int a2 = 1; a2 < NT; ++a2)
-                if (at == a2) {
-                    rho = Rt[a2];
-                    nx = Rt[a2 + 1];
-                }
-            const f32x4_t gC = Rt[NT];
+            for (int m = 0; m < GPT; ++m) gp[m] = *reinterpret_cast<const KDA_LDS f32x4_t*>(pTotW + m * DK);
+            const f32x4_t er4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sE + at * DK + ch0);   // 2^{rho_a}
+            const f32x4_t fd4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sD + at * DK + ch0);   // 2^{rho_{a+1} - rho_a}
+            const f32x4_t fc4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(sF + at * DK + ch0);   // 2^{g_C - rho_{a+1}}
             float fd[4], fc[4], er[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                fd[e] = fast_exp2(nx[e] - rho[e]);   // 2^{rho_{a+1} - rho_a}
-                fc[e] = fast_exp2(gC[e] - nx[e]);    // 2^{g_C - rho_{a+1}}
-                er[e] = fast_exp2(rho[e]);           // 2^{rho_a}
-                gam4[e] = fast_exp2(gC[e]);
-            }
-            // table 2^{rho_{a+1} - rho_a}: row a formed by the first segment of tile a
-            if (sg % (NSEG / NT) == 0) {
-                const int ta = sg / (NSEG / NT);
-                f32x4_t r0 = Rt[0], r1 = Rt[1];
-#pragma unroll
-                for (int a2 = 1; a2 < NT; ++a2)
-                    if (ta == a2) {
-                        r0 = Rt[a2];
-                        r1 = Rt[a2 + 1];
-                    }
-                f32x4_t d4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) d4[e] = fast_exp2(r1[e] - r0[e]);
-                *reinterpret_cast<KDA_LDS f32x4_t*>(pDch + ta * DK) = d4;
+                fd[e] = fd4[e];
+                fc[e] = fc4[e];
+                er[e] = er4[e];
             }
 #pragma unroll
             for (int i = 0; i < TPS; ++i) {
@@ -467,7 +464,14 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
             if constexpr (TPS == 8)
                 *reinterpret_cast<KDA_LDS u32x2_t*>(pKp1 + e * PT) = u32x2_t{kp[e][2], kp[e][3]};
         }
-        if (sg == 0) *reinterpret_cast<KDA_LDS f32x4_t*>(sGam + ch0) = gam4;
+        if (sg == 0)
+            *reinterpret_cast<KDA_LDS f32x4_t*>(sGam + ch0) = *reinterpret_cast<const KDA_LDS f32x4_t*>(sE + NT * DK + ch0);
+        // A of the next chunk (its prefix pass opens the next iteration)
+        if (c + 1 < nchunks) {
+#pragma unroll
+            for (int i = 0; i < TPS; ++i) reg_pin(pla[i]);
+            phase_a(c0 + C);
+        }
         prefetch(4, c, c0);
     }
     // the state waves run the last chunk
