@@ -385,8 +385,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": prefill_kernel_name(),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": profiled_traffic("kda_prefill_kernel_model_width.md",
-                                                 ["kda_prefill_kernel.h", "kda_device.h"]),
+                     "traffic": profiled_traffic("kda_prefill_pipe_kernel_model_width.md",
+                                                 ["kda_prefill_pipe.h", "kda_prefill_kernel.h", "kda_device.h"]),
                      "alg_bytes_per_launch": alg_bytes, "launch_ms": launch_s * 1e3,
                      "useful_tflops": useful_tflops,
                      "useful_frac_of_bf16_peak": useful_tflops / BF16_PEAK_TFLOPS},

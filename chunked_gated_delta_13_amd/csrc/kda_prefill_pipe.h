@@ -53,15 +53,17 @@ struct PipeCfg {
     static constexpr int PDB = 16 * PD + 16;
     static constexpr int VROWS = NCTH / 16;      // value rows per pass of the chunk threads
     static constexpr int NVV = C / VROWS;        // 16-byte value vectors per chunk thread
-    // Interval (1..4, at its end) in which the next chunk's decay input, q, k and v + beta are
-    // requested.  Each is requested only after the current chunk's copy is consumed.  Measured
-    // on the model-width workload: requests kept out of interval 2 (where the outputs are
-    // stored and A' runs) and mostly late in the chunk are fastest; the decay input, consumed
-    // first, goes right after phase A.
-    static constexpr int LD_LA = 1;
-    static constexpr int LD_Q = 4;
-    static constexpr int LD_K = 4;
-    static constexpr int LD_VB = NCW == 8 ? 4 : 3;
+    // Interval (1..4, at its end) of the current chunk in which each row of the next chunk's
+    // inputs is requested, 4 bits per row (row i in bits 4i..4i+3): decay input (consumed by
+    // phase A in interval 4: 1..3), q and k (consumed by A' in the next interval 2: 2..4), the
+    // value vectors and beta (handed over in the next interval 2: 2..4).  Spreading the requests
+    // keeps the vector-memory queue from filling in one burst; measured on the model-width
+    // workload.
+    static constexpr uint32_t LD_LA = 0x11111111u;
+    static constexpr uint32_t LD_Q = 0x44444444u;
+    static constexpr uint32_t LD_K = 0x44444444u;
+    static constexpr uint32_t LD_V = NCW == 8 ? 0x44444444u : 0x33333333u;
+    static constexpr int LD_B = NCW == 8 ? 4 : 3;
 
     // state-wave operands of one chunk (written by the chunk waves, read by the state waves)
     static constexpr size_t oQt = 0;
@@ -88,13 +90,21 @@ struct PipeCfg {
     static_assert(oB + 2 * C * PT - oKpT < 65536 && oKd + 2 * C * PK - oLq < 65536, "immediate offsets");
 };
 
-// Chunk wave that forms the pi-th tile pair: each takes about the same work (diagonal pairs are
-// the cheapest, pairs far below the diagonal the dearest).
+// Chunk wave that forms the pi-th tile pair (pairs enumerated row by row), and the interval it
+// does so in.  Diagonal pairs are the cheapest, pairs far below the diagonal the dearest.  The
+// diagonal pairs feed the inverses of interval 4 and stay in interval 3; with 8 chunk waves two
+// off-diagonal pairs move to interval 4 on waves that do not invert, so that interval 3 holds
+// one pair per wave.
 template <int NCW>
 constexpr int pipe_pair_owner(int pi) {
     constexpr int own4[10] = {0, 2, 3, 1, 2, 3, 0, 1, 3, 2};
-    constexpr int own8[10] = {0, 1, 2, 3, 4, 5, 6, 7, 5, 2};
+    constexpr int own8[10] = {0, 4, 1, 6, 5, 2, 4, 5, 7, 3};
     return NCW == 4 ? own4[pi] : own8[pi];
+}
+template <int NCW>
+constexpr int pipe_pair_interval(int pi) {
+    constexpr int iv8[10] = {3, 4, 3, 3, 4, 3, 3, 3, 3, 3};
+    return NCW == 4 ? 3 : iv8[pi];
 }
 
 // Unit (sequence b, head h, segment s) of one workgroup and its token range.
@@ -184,50 +194,34 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
     u32x4_t pv[NVV];
     float pbeta = 0.0f;
     auto last_row = [&](long long c0) { return (int)(t_end - 1 - c0 < C - 1 ? t_end - 1 - c0 : C - 1); };
-    auto load_la = [&](long long c0) {
+    // requests for the rows of chunk c0 whose schedule entry is iv
+    auto load_rows = [&](long long c0, int iv) {
         const int last = last_row(c0);
         const char* bl = gla + c0 * HDL;
-#pragma unroll
-        for (int i = 0; i < TPS; ++i) {
-            const uint32_t r = (uint32_t)min(sg * TPS + i, last);
-            pla[i] = *reinterpret_cast<const LaRaw*>(at_byte(bl, pinned_u(r * HDL32 + (uint32_t)(ch0 * LAE))));
-        }
-    };
-    auto load_q = [&](long long c0) {
-        const int last = last_row(c0);
         const TIn* bq = gq + c0 * HD;
-#pragma unroll
-        for (int i = 0; i < TPS; ++i) {
-            const uint32_t r = (uint32_t)min(sg * TPS + i, last);
-            pq[i] = QI::load(at_byte(bq, pinned_u(r * HD2 + (uint32_t)(ch0 * 2))));
-        }
-    };
-    auto load_k = [&](long long c0) {
-        const int last = last_row(c0);
         const TIn* bk = gk + c0 * HD;
-#pragma unroll
-        for (int i = 0; i < TPS; ++i) {
-            const uint32_t r = (uint32_t)min(sg * TPS + i, last);
-            pk[i] = QI::load(at_byte(bk, pinned_u(r * HD2 + (uint32_t)(ch0 * 2))));
-        }
-    };
-    auto load_vb = [&](long long c0) {
-        const int last = last_row(c0);
-        pbeta = *at_byte(gbeta + c0 * a.H, pinned_u((uint32_t)min(tid % C, last) * (uint32_t)(a.H * 4)));
         const TIn* bv = gv + c0 * HD;
 #pragma unroll
-        for (int m = 0; m < NVV; ++m) {
-            const uint32_t r = (uint32_t)min(v_row + VROWS * m, last);
-            pv[m] = *reinterpret_cast<const u32x4_t*>(at_byte(bv, pinned_u(r * HD2 + (uint32_t)(v_off * 2))));
+        for (int i = 0; i < TPS; ++i) {
+            const uint32_t r = (uint32_t)min(sg * TPS + i, last);
+            if (((Cfg::LD_LA >> (4 * i)) & 15) == (uint32_t)iv)
+                pla[i] = *reinterpret_cast<const LaRaw*>(at_byte(bl, pinned_u(r * HDL32 + (uint32_t)(ch0 * LAE))));
+            if (((Cfg::LD_Q >> (4 * i)) & 15) == (uint32_t)iv) pq[i] = QI::load(at_byte(bq, pinned_u(r * HD2 + (uint32_t)(ch0 * 2))));
+            if (((Cfg::LD_K >> (4 * i)) & 15) == (uint32_t)iv) pk[i] = QI::load(at_byte(bk, pinned_u(r * HD2 + (uint32_t)(ch0 * 2))));
         }
+#pragma unroll
+        for (int m = 0; m < NVV; ++m) {
+            if (((Cfg::LD_V >> (4 * m)) & 15) == (uint32_t)iv) {
+                const uint32_t r = (uint32_t)min(v_row + VROWS * m, last);
+                pv[m] = *reinterpret_cast<const u32x4_t*>(at_byte(bv, pinned_u(r * HD2 + (uint32_t)(v_off * 2))));
+            }
+        }
+        if (Cfg::LD_B == iv)
+            pbeta = *at_byte(gbeta + c0 * a.H, pinned_u((uint32_t)min(tid % C, last) * (uint32_t)(a.H * 4)));
     };
     // next chunk's inputs due for request at the end of interval iv
     auto prefetch = [&](int iv, int c, long long c0) {
-        if (c + 1 >= u.nchunks) return;
-        if (iv == Cfg::LD_LA) load_la(c0 + C);
-        if (iv == Cfg::LD_Q) load_q(c0 + C);
-        if (iv == Cfg::LD_K) load_k(c0 + C);
-        if (iv == Cfg::LD_VB) load_vb(c0 + C);
+        if (c + 1 < u.nchunks) load_rows(c0 + C, iv);
     };
 
     // A: log2-decay summed inside decay groups of G tokens (g, kept in registers until A');
@@ -298,13 +292,64 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
         }
     };
     static_assert(16 / G == Cfg::SPT && NT * Cfg::SPT == 16, "16 decay groups per chunk");
+    static_assert(TPS <= 8 && NVV <= 8, "4-bit schedule entries per row");
+
+    // B: decay-weighted KK^T and QK^T tiles of the pairs this wave forms in interval iv, one
+    // dense product per tile pair
+    auto tile_pairs = [&](int iv) {
+            constexpr int NP = NT * (NT + 1) / 2;
+            static_for<0, NP>([&](auto PIc) {
+                constexpr int pi = decltype(PIc)::value;
+                constexpr int ar = pair_row(pi);
+                constexpr int ac = pi - ar * (ar + 1) / 2;
+                if (pipe_pair_owner<NCW>(pi) != wave || pipe_pair_interval<NCW>(pi) != iv) return;   // wave-uniform
+                f32x4_t accA = zero4(), accB = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    Frag<OpT> fk, fq, fr;
+                    frag_ld(fk, pK + eLk + 16 * ar * PK + 32 * kb);
+                    frag_ld(fq, pK + 16 * ar * PK + 32 * kb);
+                    frag_ld(fr, pK + eKd + 16 * ac * PK + 32 * kb);
+                    if constexpr (ac < ar) {
+                        // R = Kd 2^{rho_ar - rho_ac}, one tile step at a time
+                        float val[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) val[j] = fr.get(j);
+#pragma unroll
+                        for (int m = ac; m < ar; ++m) {
+                            float d8[8];
+                            f32x8_ld(d8, pG + m * DK + 32 * kb);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) val[j] *= d8[j];
+                        }
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) fr.set(j, val[j]);
+                    }
+                    accA = mma(fk, fr, accA);
+                    accB = mma(fq, fr, accB);
+                }
+                const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pBe + 16 * ar);
+                if constexpr (ac == ar) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int rl = 4 * lg + j;
+                        pAd[ar * PDB + j * PD] = (lr < rl) ? accA[j] * bt4[j] : 0.0f;
+                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pW[16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(-accA[j] * bt4[j]);
+                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(accB[j]);
+                    }
+                }
+            });
+    };
 
     const int nchunks = u.nchunks;
     if (nchunks > 0) {
-        load_la(u.t_begin);
-        load_q(u.t_begin);
-        load_k(u.t_begin);
-        load_vb(u.t_begin);
+#pragma unroll
+        for (int iv = 1; iv <= 4; ++iv) load_rows(u.t_begin, iv);
         phase_a(u.t_begin);
     }
     for (int c = 0; c < nchunks; ++c) {
@@ -377,62 +422,13 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
         barrier_lds();
 
         // ---- interval 3: hand over K~ and Q~ (the state waves read the previous chunk's in
-        //      intervals 1 and 2), then B: decay-weighted KK^T and QK^T tiles, one dense product
-        //      per tile pair ----
+        //      intervals 1 and 2), then the tile pairs of B due in this interval ----
 #pragma unroll
         for (int i = 0; i < TPS; ++i) {
             QO::store_raw(pQK + i * PK, qtr[i]);
             QO::store_raw(pQK + eKt + i * PK, ktr[i]);
         }
-        {
-            constexpr int NP = NT * (NT + 1) / 2;
-            static_for<0, NP>([&](auto PIc) {
-                constexpr int pi = decltype(PIc)::value;
-                constexpr int ar = pair_row(pi);
-                constexpr int ac = pi - ar * (ar + 1) / 2;
-                if (pipe_pair_owner<NCW>(pi) != wave) return;   // wave-uniform
-                f32x4_t accA = zero4(), accB = zero4();
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    Frag<OpT> fk, fq, fr;
-                    frag_ld(fk, pK + eLk + 16 * ar * PK + 32 * kb);
-                    frag_ld(fq, pK + 16 * ar * PK + 32 * kb);
-                    frag_ld(fr, pK + eKd + 16 * ac * PK + 32 * kb);
-                    if constexpr (ac < ar) {
-                        // R = Kd 2^{rho_ar - rho_ac}, one tile step at a time
-                        float val[8];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) val[j] = fr.get(j);
-#pragma unroll
-                        for (int m = ac; m < ar; ++m) {
-                            float d8[8];
-                            f32x8_ld(d8, pG + m * DK + 32 * kb);
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) val[j] *= d8[j];
-                        }
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) fr.set(j, val[j]);
-                    }
-                    accA = mma(fk, fr, accA);
-                    accB = mma(fq, fr, accB);
-                }
-                const f32x4_t bt4 = *reinterpret_cast<const KDA_LDS f32x4_t*>(pBe + 16 * ar);
-                if constexpr (ac == ar) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int rl = 4 * lg + j;
-                        pAd[ar * PDB + j * PD] = (lr < rl) ? accA[j] * bt4[j] : 0.0f;
-                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        pW[16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(-accA[j] * bt4[j]);
-                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(accB[j]);
-                    }
-                }
-            });
-        }
+        tile_pairs(3);
         prefetch(3, c, c0);
         barrier_lds();
 
@@ -466,6 +462,7 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
         }
         if (sg == 0)
             *reinterpret_cast<KDA_LDS f32x4_t*>(sGam + ch0) = *reinterpret_cast<const KDA_LDS f32x4_t*>(sE + NT * DK + ch0);
+        tile_pairs(4);
         // A of the next chunk (its prefix pass opens the next iteration)
         if (c + 1 < nchunks) {
 #pragma unroll
