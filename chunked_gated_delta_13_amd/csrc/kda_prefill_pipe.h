@@ -46,8 +46,13 @@ struct PipeCfg {
     static constexpr int GPT = TPS / G;          // decay groups per segment
     static constexpr int SPT = 16 / G;           // decay groups per tile
     static constexpr int NCT = 2;                // 16-column tiles per state wave
-    static constexpr int PK = DK + 8;            // pitch of [C][DK] operand arrays
-    static constexpr int PT = C + 8;             // pitch of [*][C] arrays
+    // Pitches (elements).  Fragment loads are pairs of 8-byte reads 32 bytes apart; measured on
+    // gfx950 they are bank-conflict free at row pitches of 66 or 34 dwords and two-way conflicted
+    // at 68 or 36 (and four-way at 72 or 40).  K'^T keeps 72 elements: its rows are permuted
+    // (below), which makes both its transposed stores and its fragment loads conflict free.
+    static constexpr int PK = DK + 4;            // pitch of [C][DK] operand arrays (66 dwords)
+    static constexpr int PT = C + 8;             // pitch of K'^T rows
+    static constexpr int PTB = C + 4;            // pitch of the T/A and Bqk rows (34 dwords)
     static constexpr int PV = DK + 8;            // pitch of the value rows
     static constexpr int PD = 20;
     static constexpr int PDB = 16 * PD + 16;
@@ -70,8 +75,8 @@ struct PipeCfg {
     static constexpr size_t oKt = oQt + pipe_al(2 * C * PK);
     static constexpr size_t oKpT = oKt + pipe_al(2 * C * PK);
     static constexpr size_t oTA = oKpT + pipe_al(2 * DK * PT);
-    static constexpr size_t oB = oTA + pipe_al(2 * C * PT);
-    static constexpr size_t oV = oB + pipe_al(2 * C * PT);
+    static constexpr size_t oB = oTA + pipe_al(2 * C * PTB);
+    static constexpr size_t oV = oB + pipe_al(2 * C * PTB);
     static constexpr size_t oBeta = oV + pipe_al(2 * C * PV);
     static constexpr size_t oGam = oBeta + pipe_al(4 * C);
     // chunk-wave scratch
@@ -87,7 +92,8 @@ struct PipeCfg {
     static_assert(LDS <= 160 * 1024, "LDS budget of one gfx950 workgroup");
     static_assert((NCW == 4 && TPS == 8) || (NCW == 8 && TPS == 4), "segment layout of the chunk waves");
     static_assert(TPS % G == 0 && NSEG % NT == 0, "segments hold whole decay groups");
-    static_assert(oB + 2 * C * PT - oKpT < 65536 && oKd + 2 * C * PK - oLq < 65536, "immediate offsets");
+    static_assert(oB + 2 * C * PTB - oTA < 65536 && oKd + 2 * C * PK - oLq < 65536, "immediate offsets");
+    static_assert(PK % 4 == 0 && PTB % 4 == 0 && PT % 4 == 0 && PV % 8 == 0, "8-byte rows (16 for values)");
 };
 
 // Chunk wave that forms the pi-th tile pair (pairs enumerated row by row), and the interval it
@@ -129,7 +135,7 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
     using QO = Quad<OpT>;
     constexpr int DK = Cfg::DK, C = Cfg::C, NT = Cfg::NT, NQ = Cfg::NQ;
     constexpr int TPS = Cfg::TPS, G = Cfg::G, GPT = Cfg::GPT, SPT = Cfg::SPT;
-    constexpr int PK = Cfg::PK, PT = Cfg::PT, PV = Cfg::PV, PD = Cfg::PD, PDB = Cfg::PDB, NVV = Cfg::NVV;
+    constexpr int PK = Cfg::PK, PT = Cfg::PT, PTB = Cfg::PTB, PV = Cfg::PV, PD = Cfg::PD, PDB = Cfg::PDB, NVV = Cfg::NVV;
     constexpr int NSEG = Cfg::NSEG, VROWS = Cfg::VROWS;
     constexpr int NKB = DK / 32;
     constexpr int eLk = (int)((Cfg::oLk - Cfg::oLq) / 2);
@@ -165,11 +171,11 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
     KDA_LDS OpT* const pK = lds_pin(sLq + lr * PK + 4 * lg);            // fragment rows (tile pairs)
     KDA_LDS float* const pG = lds_pin(sD + 4 * lg);                     // D table by accumulator row
     KDA_LDS float* const pBe = lds_pin(sBeta + 4 * lg);                 // beta by accumulator row
-    KDA_LDS OpT* const pW = lds_pin(sTA + 4 * lg * PT + lr);            // accumulator element of TA, B
+    KDA_LDS OpT* const pW = lds_pin(sTA + 4 * lg * PTB + lr);           // accumulator element of TA, B
     KDA_LDS float* const pAd = lds_pin(sAd + 4 * lg * PD + lr);         // diagonal block, row-major
     const int wi = wave & (NT - 1);                                     // diagonal block (waves < NT)
     KDA_LDS float* const pAi = lds_pin(sAd + wi * PDB + (lane & 15) * PD);
-    KDA_LDS OpT* const pTi = lds_pin(sTA + 16 * wi * (PT + 1) + (lane & 15) * PT + (lane >> 4));
+    KDA_LDS OpT* const pTi = lds_pin(sTA + 16 * wi * (PTB + 1) + (lane & 15) * PTB + (lane >> 4));
     const int v_row = tid / 16, v_off = (tid % 16) * 8;                 // value rows: 16 vectors each
     KDA_LDS TIn* const pVc = lds_pin(sV + v_row * PV + v_off);
 
@@ -334,13 +340,13 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
                     for (int j = 0; j < 4; ++j) {
                         const int rl = 4 * lg + j;
                         pAd[ar * PDB + j * PD] = (lr < rl) ? accA[j] * bt4[j] : 0.0f;
-                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
+                        pW[eBw + 16 * ar * PTB + 16 * ac + j * PTB] = from_f32<OpT>((lr <= rl) ? accB[j] : 0.0f);
                     }
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        pW[16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(-accA[j] * bt4[j]);
-                        pW[eBw + 16 * ar * PT + 16 * ac + j * PT] = from_f32<OpT>(accB[j]);
+                        pW[16 * ar * PTB + 16 * ac + j * PTB] = from_f32<OpT>(-accA[j] * bt4[j]);
+                        pW[eBw + 16 * ar * PTB + 16 * ac + j * PTB] = from_f32<OpT>(accB[j]);
                     }
                 }
             });
@@ -486,14 +492,14 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
     using OpT = __bf16;
     using TIn = __bf16;
     constexpr int DK = Cfg::DK, C = Cfg::C, NT = Cfg::NT, NTB = Cfg::NTB, NCT = Cfg::NCT;
-    constexpr int PK = Cfg::PK, PT = Cfg::PT, PV = Cfg::PV;
+    constexpr int PK = Cfg::PK, PT = Cfg::PT, PTB = Cfg::PTB, PV = Cfg::PV;
     constexpr int NIT = DK / 16, NKB = DK / 32;
     constexpr int eKt = (int)((Cfg::oKt - Cfg::oQt) / 2);
-    constexpr int eTA = (int)((Cfg::oTA - Cfg::oKpT) / 2);
-    constexpr int eB = (int)((Cfg::oB - Cfg::oKpT) / 2);
+    constexpr int eBs = (int)((Cfg::oB - Cfg::oTA) / 2);
 
     KDA_LDS OpT* sQt = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oQt);
     KDA_LDS OpT* sKpT = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oKpT);
+    KDA_LDS OpT* sTA = reinterpret_cast<KDA_LDS OpT*>(smem + Cfg::oTA);
     KDA_LDS TIn* sV = reinterpret_cast<KDA_LDS TIn*>(smem + Cfg::oV);
     KDA_LDS float* sBeta = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oBeta);
     KDA_LDS float* sGam = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oGam);
@@ -528,7 +534,7 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
     }
 
     KDA_LDS OpT* const pQs = lds_pin(sQt + lr * PK + 4 * lg);             // fragment rows of Q~, K~
-    KDA_LDS OpT* const pTs = lds_pin(sKpT + lr * PT + 4 * lg);            // fragment rows of TA, B
+    KDA_LDS OpT* const pTs = lds_pin(sTA + lr * PTB + 4 * lg);            // fragment rows of TA, B
     // fragment rows of the permuted K'^T (row 16 it + lr holds column c at c ^ (8 it + 4 (lr >> 3))):
     // one base for even and one for odd it, the rest of the permutation is an immediate offset
     const int hsw = lr >> 3;
@@ -600,13 +606,13 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
 #pragma unroll
             for (int kb = 0; kb < ar / 2; ++kb) {
                 Frag<OpT> fa;
-                frag_ld(fa, pTs + eTA + 16 * ar * PT + 32 * kb);
+                frag_ld(fa, pTs + 16 * ar * PTB + 32 * kb);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) W[ct] = mma(fa, fU[kb][ct], W[ct]);
             }
             if (ar & 1) {
                 Frag<OpT> fa;
-                frag_ld_lo(fa, pTs + eTA + 16 * ar * PT + 16 * (ar - 1));
+                frag_ld_lo(fa, pTs + 16 * ar * PTB + 16 * (ar - 1));
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     Frag<OpT> fb;
@@ -615,7 +621,7 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
                 }
             }
             Frag<OpT> ft;
-            frag_ld_lo(ft, pTs + eTA + 16 * ar * PT + 16 * ar);
+            frag_ld_lo(ft, pTs + 16 * ar * PTB + 16 * ar);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 Frag<OpT> fw;
@@ -656,7 +662,7 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
 #pragma unroll
                 for (int kb = 0; kb <= ar / 2; ++kb) {
                     Frag<OpT> fb;
-                    frag_ld(fb, pTs + eB + 16 * ar * PT + 32 * kb);
+                    frag_ld(fb, pTs + eBs + 16 * ar * PTB + 32 * kb);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) O[ct] = mma(fU[kb][ct], fb, O[ct]);
                 }
@@ -728,7 +734,7 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
 template <int NCW, bool GATE>
 __global__ __launch_bounds__(64 * (NCW + 4)) void kda_prefill_pipe_kernel(const PrefillArgs a) {
     using Cfg = PipeCfg<NCW>;
-    constexpr int C = Cfg::C, PT = Cfg::PT, DK = Cfg::DK, NTH = Cfg::NTH;
+    constexpr int C = Cfg::C, PT = Cfg::PT, PTB = Cfg::PTB, DK = Cfg::DK, NTH = Cfg::NTH;
     __shared__ __align__(16) char smem_[Cfg::LDS];
     KDA_LDS char* smem = (KDA_LDS char*)smem_;
 
@@ -756,7 +762,7 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void kda_prefill_pipe_kernel(const 
         KDA_LDS __bf16* sKpT = reinterpret_cast<KDA_LDS __bf16*>(smem + Cfg::oKpT);
         KDA_LDS __bf16* sTA = reinterpret_cast<KDA_LDS __bf16*>(smem + Cfg::oTA);
         KDA_LDS __bf16* sB = reinterpret_cast<KDA_LDS __bf16*>(smem + Cfg::oB);
-        for (int e = tid; e < C * PT; e += NTH) {
+        for (int e = tid; e < C * PTB; e += NTH) {
             sTA[e] = from_f32<__bf16>(0.0f);
             sB[e] = from_f32<__bf16>(0.0f);
         }
