@@ -58,8 +58,10 @@ struct PrefillCfg {
     static constexpr int SPT = 16 / G;           // decay groups per 16-token tile
     static constexpr int CP = C < 32 ? 32 : C;   // token extent of token-indexed rows
     static constexpr int PADE = sizeof(OpT) == 2 ? 8 : 4;
-    static constexpr int PK = DK + PADE;         // pitch of [C][DK] operand arrays
-    static constexpr int PT = CP + PADE;         // pitch of sTA, sB, sKpT
+    // Row pitches: a bf16 fragment load is two 8-byte reads 32 bytes apart, bank-conflict free
+    // on gfx950 at row pitches of 66 or 34 dwords (two-way conflicted at 68 or 36).
+    static constexpr int PK = DK + 4;            // pitch of [C][DK] operand arrays
+    static constexpr int PT = CP + (sizeof(OpT) == 2 && CP == 64 ? 4 : PADE);   // pitch of sTA, sB, sKpT
     static constexpr int PV = DVW + PADE;        // pitch of sV
     static constexpr int PW = 16 * NCT + PADE;   // pitch of a wave's output staging
     static constexpr int PD = 20;                // pitch of the transposed fp32 diagonal A blocks
