@@ -13,9 +13,12 @@
 //   e  = v - p
 //   S  = S' + beta k e^T                     written back from registers
 //   o  = S^T q = r + beta (k . q) e          no second pass over S
-// A workgroup owns (sequence, head, 64 state columns): 16 column groups of 4
-// (float4, 256 contiguous bytes per row) x 16 row groups.  Column sums are
-// reduced across row groups with lane shuffles, then across the 4 waves in LDS.
+// A workgroup owns one whole (sequence, head) state: DV/4 column groups of 4 (float4, so
+// each state row is read as one contiguous run) x 16 row groups.  Column sums are reduced
+// across the row groups of a wave with lane shuffles, then across the waves in LDS.  The
+// state a workgroup takes is chosen so that each of the 8 XCDs (which receive workgroups
+// round-robin) streams one contiguous range of states: a whole-state, XCD-contiguous
+// pattern moves measurably more bytes per second through HBM than half-state workgroups.
 // For an m-token block the state is read once, the m tokens run in order on
 // chip, and the state is written back only when the block is committed
 // ("Kimi K3's architecture", "The bill comes due in the serving stack": the
@@ -27,12 +30,15 @@ namespace kda {
 
 // MM = most tokens per block this instantiation stages (1 for the decode step).
 template <int DK, typename TIn, int MM>
-__global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(4 * DK) void kda_decode_kernel(const DecodeArgs a, int per_xcd) {
     constexpr int DV = DK;
-    constexpr int NVB = DV / 64;     // 64-column blocks per state
-    constexpr int RPT = DK / 16;     // state rows per thread
-    const long long nh = blockIdx.x / NVB;
-    const int vb = blockIdx.x % NVB;
+    constexpr int NCG = DV / 4;      // float4 column groups per state row
+    constexpr int NRG = 16;          // row groups
+    constexpr int NTH = NCG * NRG;   // threads per workgroup (4 * DK)
+    constexpr int NW = NTH / 64;     // waves per workgroup
+    constexpr int RPT = DK / NRG;    // state rows per thread
+    static_assert(NCG <= 64 && 64 % NCG == 0, "a wave holds whole row groups");
+    const long long nh = (long long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (nh >= a.NH) return;
     const long long n = nh / a.H;
     const int h = (int)(nh % a.H);
@@ -43,47 +49,47 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeArgs a) {
     }
     if (mt == 0) return;             // nothing to run: the state stays as it is
     const int tid = threadIdx.x;
-    const int cg = tid & 15, rg = tid >> 4;
+    const int cg = tid % NCG, rg = tid / NCG;
     const int lane = tid & 63, wave = tid >> 6;
-    const int col = vb * 64 + cg * 4;
+    const int col = cg * 4;
 
     float* Sb = a.S + nh * (long long)(DK * DV) + col;
     f32x4_t s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
-        s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(Sb + (long long)(rg + 16 * m) * DV));
+        s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(Sb + (long long)(rg + NRG * m) * DV));
 
     // A block's token inputs are staged in LDS once, while the state loads are in flight; a
     // single token (the decode step) is read straight from memory.
     constexpr int MS = MM > 1 ? MM : 1;
-    __shared__ float skk[MS][DK], sqq[MS][DK], sal[MS][DK], sv[MS][64], sbt[MS];
+    __shared__ float skk[MS][DK], sqq[MS][DK], sal[MS][DK], sv[MS][DV], sbt[MS];
     auto tok_of = [&](int t) { return (n * a.m + t) * a.H + h; };   // token row of [N, m, H, *]
     auto alpha_of = [](float la) { return __expf(fminf(fmaxf(la, kLogAlphaMin), 0.0f)); };
     if constexpr (MM > 1) {
-        for (int e = tid; e < mt * DK; e += 256) {
+        for (int e = tid; e < mt * DK; e += NTH) {
             const int t = e / DK, i = e % DK;
             const long long base = tok_of(t) * DK + i;
             skk[t][i] = to_f32<TIn>(reinterpret_cast<const TIn*>(a.k)[base]);
             sqq[t][i] = to_f32<TIn>(reinterpret_cast<const TIn*>(a.q)[base]);
             sal[t][i] = alpha_of(a.log_alpha[base]);
         }
-        for (int e = tid; e < mt * 64; e += 256) {
-            const int t = e / 64, c = e % 64;
-            sv[t][c] = to_f32<TIn>(reinterpret_cast<const TIn*>(a.v)[tok_of(t) * DV + vb * 64 + c]);
+        for (int e = tid; e < mt * DV; e += NTH) {
+            const int t = e / DV, c = e % DV;
+            sv[t][c] = to_f32<TIn>(reinterpret_cast<const TIn*>(a.v)[tok_of(t) * DV + c]);
         }
         if (tid < mt) sbt[tid] = a.beta[tok_of(tid)];
     }
 
-    // column sums of the 4 waves, double-buffered over tokens so one barrier per token suffices
-    __shared__ f32x4_t sp[2][4][16], sr[2][4][16];
-    __shared__ float skq[2][4];
+    // per-wave column sums, then the workgroup totals (p, then r, then k.q)
+    __shared__ __attribute__((aligned(16))) float spart[NW][2 * DV + 4];
+    __shared__ float stot[2 * DV + 1];
     if constexpr (MM > 1) __syncthreads();
 
     for (int t = 0; t < mt; ++t) {
         float kk[RPT], qq[RPT], al[RPT];
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
-            const int i = rg + 16 * m;
+            const int i = rg + NRG * m;
             if constexpr (MM > 1) {
                 kk[m] = skk[t][i];
                 qq[m] = sqq[t][i];
@@ -108,9 +114,9 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeArgs a) {
             }
             kq += kk[m] * qq[m];
         }
-        // reduce over the 4 row groups of this wave (lanes 16 apart) ...
+        // reduce over the row groups of this wave (lanes NCG apart) ...
 #pragma unroll
-        for (int off = 16; off < 64; off <<= 1) {
+        for (int off = NCG; off < 64; off <<= 1) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 p[j] += __shfl_xor(p[j], off);
@@ -118,17 +124,29 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeArgs a) {
             }
             kq += __shfl_xor(kq, off);
         }
-        // ... then over the 4 waves
-        const int bsel = t & 1;
-        if (lane < 16) {
-            sp[bsel][wave][cg] = p;
-            sr[bsel][wave][cg] = r;
+        // ... then over the waves: thread i <= 2 DV sums value i over the waves in order.  Two
+        // barriers per token keep the partials and totals single-buffered.
+        if (lane < NCG) {
+            *reinterpret_cast<f32x4_t*>(&spart[wave][col]) = p;
+            *reinterpret_cast<f32x4_t*>(&spart[wave][DV + col]) = r;
         }
-        if (lane == 0) skq[bsel][wave] = kq;
+        if (lane == 0) spart[wave][2 * DV] = kq;
         __syncthreads();
-        p = sp[bsel][0][cg] + sp[bsel][1][cg] + sp[bsel][2][cg] + sp[bsel][3][cg];
-        r = sr[bsel][0][cg] + sr[bsel][1][cg] + sr[bsel][2][cg] + sr[bsel][3][cg];
-        kq = skq[bsel][0] + skq[bsel][1] + skq[bsel][2] + skq[bsel][3];
+        if (tid <= 2 * DV) {
+            float acc = spart[0][tid];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) acc += spart[w][tid];
+            stot[tid] = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] = stot[col + j];
+        const bool writes_o = a.o && rg == 0;
+        if (writes_o) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[j] = stot[DV + col + j];
+            kq = stot[2 * DV];
+        }
 
         float bt;
         f32x4_t e;
@@ -148,7 +166,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) s[m][j] += bk * e[j];
         }
-        if (a.o && rg == 0) {
+        if (writes_o) {
             TIn* on = reinterpret_cast<TIn*>(a.o) + tok_of(t) * DV + col;
             const float bkq = bt * kq;
 #pragma unroll
@@ -158,17 +176,18 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const DecodeArgs a) {
     if (a.write_state) {
 #pragma unroll
         for (int m = 0; m < RPT; ++m)
-            __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4_t*>(Sb + (long long)(rg + 16 * m) * DV));
+            __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4_t*>(Sb + (long long)(rg + NRG * m) * DV));
     }
 }
 
 template <int MM>
-static hipError_t launch_decode_mm(int dk, bool f32, const DecodeArgs& a, dim3 grid, hipStream_t stream) {
-    const dim3 block(256);
-    if (dk == 128 && !f32) hipLaunchKernelGGL((kda_decode_kernel<128, __bf16, MM>), grid, block, 0, stream, a);
-    else if (dk == 128 && f32) hipLaunchKernelGGL((kda_decode_kernel<128, float, MM>), grid, block, 0, stream, a);
-    else if (dk == 64 && !f32) hipLaunchKernelGGL((kda_decode_kernel<64, __bf16, MM>), grid, block, 0, stream, a);
-    else if (dk == 64 && f32) hipLaunchKernelGGL((kda_decode_kernel<64, float, MM>), grid, block, 0, stream, a);
+static hipError_t launch_decode_mm(int dk, bool f32, const DecodeArgs& a, dim3 grid, int per_xcd,
+                                   hipStream_t stream) {
+    const dim3 block(4 * dk);
+    if (dk == 128 && !f32) hipLaunchKernelGGL((kda_decode_kernel<128, __bf16, MM>), grid, block, 0, stream, a, per_xcd);
+    else if (dk == 128 && f32) hipLaunchKernelGGL((kda_decode_kernel<128, float, MM>), grid, block, 0, stream, a, per_xcd);
+    else if (dk == 64 && !f32) hipLaunchKernelGGL((kda_decode_kernel<64, __bf16, MM>), grid, block, 0, stream, a, per_xcd);
+    else if (dk == 64 && f32) hipLaunchKernelGGL((kda_decode_kernel<64, float, MM>), grid, block, 0, stream, a, per_xcd);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -176,12 +195,13 @@ static hipError_t launch_decode_mm(int dk, bool f32, const DecodeArgs& a, dim3 g
 hipError_t launch_decode(int dk, bool f32, const DecodeArgs& a, hipStream_t stream) {
     if (a.NH <= 0) return hipSuccess;
     if (a.m < 1 || a.m > kDecodeMaxTokens) return hipErrorInvalidValue;
-    const long long nblk = a.NH * (dk / 64);
-    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)nblk);
-    if (a.m == 1) return launch_decode_mm<1>(dk, f32, a, grid, stream);
-    if (a.m <= 4) return launch_decode_mm<4>(dk, f32, a, grid, stream);
-    return launch_decode_mm<kDecodeMaxTokens>(dk, f32, a, grid, stream);
+    // one workgroup per state; workgroup b takes state (b % 8) * per_xcd + b / 8
+    const long long per_xcd = (a.NH + 7) / 8;
+    if (per_xcd > 0x7fffffffLL / 8) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(8 * per_xcd));
+    if (a.m == 1) return launch_decode_mm<1>(dk, f32, a, grid, (int)per_xcd, stream);
+    if (a.m <= 4) return launch_decode_mm<4>(dk, f32, a, grid, (int)per_xcd, stream);
+    return launch_decode_mm<kDecodeMaxTokens>(dk, f32, a, grid, (int)per_xcd, stream);
 }
 
 }  // namespace kda
