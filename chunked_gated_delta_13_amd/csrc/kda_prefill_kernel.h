@@ -93,7 +93,7 @@ struct PrefillCfg {
     static constexpr size_t oAd = oB + al(sizeof(OpT) * C * PT);
     static constexpr size_t oE = oAd + al(4 * NT * PDB);
     static constexpr size_t oD = oE + al(4 * (NT + 1) * DK);
-    static constexpr size_t oBeta = oD + al(4 * NT * DK);
+    static constexpr size_t oBeta = oD + al(4 * (NT == 4 ? NT + 3 : NT) * DK);   // D rows (+ products)
     static constexpr size_t oTot = oBeta + al(4 * C);
     static constexpr size_t oO = oTot + al(4 * 16 * DK);
     static constexpr size_t LDS = oO + al(sizeof(TIn) * NW * 16 * PW);
@@ -503,6 +503,25 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                     }
                     *reinterpret_cast<KDA_LDS f32x4_t*>(pCh + t2 * DK) = e4;
                     if (t2 < NT) *reinterpret_cast<KDA_LDS f32x4_t*>(pCh + fD + t2 * DK) = d4;
+                    if constexpr (NT == 4) {
+                        // after the D rows: D_0 D_1, D_1 D_2 and (D_0 D_1) D_2, which scale the
+                        // tile pairs two and three tiles below the diagonal
+                        if (t2 == NT) {
+                            f32x4_t p01, p12, p012;
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                const float d0 = fast_exp2(Rt[1][u] - Rt[0][u]);
+                                const float d1 = fast_exp2(Rt[2][u] - Rt[1][u]);
+                                const float d2 = fast_exp2(Rt[3][u] - Rt[2][u]);
+                                p01[u] = d0 * d1;
+                                p12[u] = d1 * d2;
+                                p012[u] = p01[u] * d2;
+                            }
+                            *reinterpret_cast<KDA_LDS f32x4_t*>(pCh + fD + NT * DK) = p01;
+                            *reinterpret_cast<KDA_LDS f32x4_t*>(pCh + fD + (NT + 1) * DK) = p12;
+                            *reinterpret_cast<KDA_LDS f32x4_t*>(pCh + fD + (NT + 2) * DK) = p012;
+                        }
+                    }
                 }
             }
             float kp[4][TPS];   // K' of this thread's channels, by channel: one vector store each
@@ -561,18 +580,18 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                     if constexpr (!DUAL) frag_ld(fq, pK + 16 * ar * PK + 32 * kb);
                     frag_ld(fr, pK + eKd + 16 * ac * PK + 32 * kb);
                     if constexpr (ac < ar) {
-                        // R = Kd 2^{rho_ar - rho_ac}: multiply by 2^{rho_{m+1} - rho_m} one tile at a
-                        // time, the first step bringing Kd (up to 2^115) down to at most 1
-                        float val[8];
+                        // R = Kd 2^{rho_ar - rho_ac}: one multiply by D_ac = 2^{rho_{ac+1} - rho_ac}
+                        // or, two or three tiles below the diagonal, by the product row
+                        // D_ac ... D_{ar-1} (formed left to right).  Where that product underflows,
+                        // the exact R is below 2^{115.4 - 149}: far under the operands' bf16 step.
+                        static_assert(ar - ac == 1 || NT == 4, "product rows exist for four row tiles");
+                        constexpr int prow = (ar - ac == 1) ? ac : (ar - ac == 2 ? NT + ac : NT + 2);
+                        float val[8], d8[8];
 #pragma unroll
                         for (int j = 0; j < 8; ++j) val[j] = fr.get(j);
+                        f32x8_ld(d8, pG + fD + prow * DK + 32 * kb);
 #pragma unroll
-                        for (int m = ac; m < ar; ++m) {
-                            float d8[8];
-                            f32x8_ld(d8, pG + fD + m * DK + 32 * kb);
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) val[j] *= d8[j];
-                        }
+                        for (int j = 0; j < 8; ++j) val[j] *= d8[j];
 #pragma unroll
                         for (int j = 0; j < 8; ++j) fr.set(j, val[j]);
                     }

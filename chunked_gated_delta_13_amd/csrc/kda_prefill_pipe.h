@@ -85,11 +85,12 @@ struct PipeCfg {
     static constexpr size_t oKd = oLk + pipe_al(2 * C * PK);
     static constexpr size_t oTot = oKd + pipe_al(2 * C * PK);
     static constexpr size_t oD = oTot + pipe_al(4 * 16 * DK);
-    static constexpr size_t oE = oD + pipe_al(4 * NT * DK);
+    static constexpr size_t oE = oD + pipe_al(4 * (NT + 3) * DK);   // D rows, then the products
     static constexpr size_t oF = oE + pipe_al(4 * (NT + 1) * DK);
     static constexpr size_t oAd = oF + pipe_al(4 * NT * DK);
     static constexpr size_t LDS = oAd + pipe_al(4 * NT * PDB);
     static_assert(LDS <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    static_assert(NT == 4, "the D table's product rows cover pairs up to three tiles apart");
     static_assert((NCW == 4 && TPS == 8) || (NCW == 8 && TPS == 4), "segment layout of the chunk waves");
     static_assert(TPS % G == 0 && NSEG % NT == 0, "segments hold whole decay groups");
     static_assert(oB + 2 * C * PTB - oTA < 65536 && oKd + 2 * C * PK - oLq < 65536, "immediate offsets");
@@ -267,8 +268,9 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
     // Prefix pass, one channel per thread (threads 0..DK-1): from the group totals, in the
     // canonical order (group totals in order inside a tile, tile totals in order across the
     // chunk), rho_a for every tile and, in place of each group total, the sum of the groups
-    // before it inside its tile; then the tables 2^{rho_a} (a = 0..NT), 2^{rho_{a+1} - rho_a}
-    // and 2^{g_C - rho_{a+1}}.
+    // before it inside its tile; then the tables 2^{rho_a} (a = 0..NT), D_a = 2^{rho_{a+1} - rho_a}
+    // and 2^{g_C - rho_{a+1}}, and after the D rows the products D_0 D_1, D_1 D_2, (D_0 D_1) D_2
+    // that scale the tile pairs two and three tiles below the diagonal.
     auto prefix_pass = [&]() {
         const int ch = tid;
         float tot[16];
@@ -291,11 +293,17 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
         }
 #pragma unroll
         for (int a2 = 0; a2 <= NT; ++a2) sE[a2 * DK + ch] = fast_exp2(Rt[a2]);
+        float dd[NT];
 #pragma unroll
         for (int a2 = 0; a2 < NT; ++a2) {
-            sD[a2 * DK + ch] = fast_exp2(Rt[a2 + 1] - Rt[a2]);
+            dd[a2] = fast_exp2(Rt[a2 + 1] - Rt[a2]);
+            sD[a2 * DK + ch] = dd[a2];
             sF[a2 * DK + ch] = fast_exp2(Rt[NT] - Rt[a2 + 1]);
         }
+        const float d01 = dd[0] * dd[1];
+        sD[NT * DK + ch] = d01;
+        sD[(NT + 1) * DK + ch] = dd[1] * dd[2];
+        sD[(NT + 2) * DK + ch] = d01 * dd[2];
     };
     static_assert(16 / G == Cfg::SPT && NT * Cfg::SPT == 16, "16 decay groups per chunk");
     static_assert(TPS <= 8 && NVV <= 8, "4-bit schedule entries per row");
@@ -317,17 +325,14 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
                     frag_ld(fq, pK + 16 * ar * PK + 32 * kb);
                     frag_ld(fr, pK + eKd + 16 * ac * PK + 32 * kb);
                     if constexpr (ac < ar) {
-                        // R = Kd 2^{rho_ar - rho_ac}, one tile step at a time
-                        float val[8];
+                        // R = Kd 2^{rho_ar - rho_ac}: one multiply by D_ac or by a product row
+                        constexpr int prow = (ar - ac == 1) ? ac : (ar - ac == 2 ? NT + ac : NT + 2);
+                        float val[8], d8[8];
 #pragma unroll
                         for (int j = 0; j < 8; ++j) val[j] = fr.get(j);
+                        f32x8_ld(d8, pG + prow * DK + 32 * kb);
 #pragma unroll
-                        for (int m = ac; m < ar; ++m) {
-                            float d8[8];
-                            f32x8_ld(d8, pG + m * DK + 32 * kb);
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) val[j] *= d8[j];
-                        }
+                        for (int j = 0; j < 8; ++j) val[j] *= d8[j];
 #pragma unroll
                         for (int j = 0; j < 8; ++j) fr.set(j, val[j]);
                     }
@@ -565,15 +570,14 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
             for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = zero4();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            Frag<OpT> fs[NCT];
+            Frag<OpT> fk[NT], fs[NCT];
+#pragma unroll
+            for (int ar = 0; ar < NT; ++ar) frag_ld(fk[ar], pQs + eKt + 16 * ar * PK + 32 * kb);
             s_frag(fs, kb);
 #pragma unroll
-            for (int ar = 0; ar < NT; ++ar) {
-                Frag<OpT> fk;
-                frag_ld(fk, pQs + eKt + 16 * ar * PK + 32 * kb);
+            for (int ar = 0; ar < NT; ++ar)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = mma(fk, fs[ct], Rh[ar][ct]);
-            }
+                for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = mma(fk[ar], fs[ct], Rh[ar][ct]);
         }
 #pragma unroll
         for (int ar = 0; ar < NT; ++ar) {
@@ -644,15 +648,14 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
                 for (int ct = 0; ct < NCT; ++ct) Oa[ar][ct] = zero4();
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                Frag<OpT> fs[NCT];
+                Frag<OpT> fq[NT], fs[NCT];
+#pragma unroll
+                for (int ar = 0; ar < NT; ++ar) frag_ld(fq[ar], pQs + 16 * ar * PK + 32 * kb);
                 s_frag(fs, kb);
 #pragma unroll
-                for (int ar = 0; ar < NT; ++ar) {
-                    Frag<OpT> fq;
-                    frag_ld(fq, pQs + 16 * ar * PK + 32 * kb);
+                for (int ar = 0; ar < NT; ++ar)
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) Oa[ar][ct] = mma(fs[ct], fq, Oa[ar][ct]);
-                }
+                    for (int ct = 0; ct < NCT; ++ct) Oa[ar][ct] = mma(fs[ct], fq[ar], Oa[ar][ct]);
             }
 #pragma unroll
             for (int ar = 0; ar < NT; ++ar) {
