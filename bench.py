@@ -35,15 +35,18 @@ BYTES_PER_TOKEN_HEAD = 1540
 # Useful multiply-adds per token-head: five lower-triangular 16-token-tile products
 # (5 * (n+1)/2 * 16 * d with n = 4) + three state products (3 d^2) + the inverse (~1067).
 FLOPS_PER_TOKEN_HEAD = 2 * (5 * 2.5 * 16 * 128 + 3 * 128 * 128 + 1067)
+# sources of the model-width prefill kernel (a profile's counters hold while their hash matches)
+PREFILL_SOURCES = ["kda_prefill_pipe.h", "kda_prefill_kernel.h", "kda_device.h"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def profiled_traffic(summary, sources):
-    """HBM bytes per launch recorded in profiles/<summary> from rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
-    or None when the kernel sources have changed since those counters were taken."""
+def profiled_value(summary, sources, key="traffic_bytes_per_launch"):
+    """A figure recorded in profiles/<summary> from rocprofv3 PMC runs (HBM bytes per launch from
+    FETCH_SIZE/WRITE_SIZE, or the MFMA busy fraction), or None when the kernel sources have
+    changed since those counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
@@ -60,7 +63,7 @@ def profiled_traffic(summary, sources):
     if rec.get("source_sha256_16") != h.hexdigest()[:16]:
         return None
     try:
-        return float(rec["traffic_bytes_per_launch"])
+        return float(rec[key])
     except (KeyError, ValueError):
         return None
 
@@ -385,8 +388,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": prefill_kernel_name(),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": profiled_traffic("kda_prefill_pipe_kernel_model_width.md",
-                                                 ["kda_prefill_pipe.h", "kda_prefill_kernel.h", "kda_device.h"]),
+                     "traffic": profiled_value("kda_prefill_pipe_kernel_model_width.md", PREFILL_SOURCES),
+                     "mfma_busy_frac_rocprof": profiled_value("kda_prefill_pipe_kernel_model_width.md",
+                                                              PREFILL_SOURCES, "mfma_busy_frac"),
                      "alg_bytes_per_launch": alg_bytes, "launch_ms": launch_s * 1e3,
                      "useful_tflops": useful_tflops,
                      "useful_frac_of_bf16_peak": useful_tflops / BF16_PEAK_TFLOPS},
@@ -410,8 +414,8 @@ def main():
                             "us_per_step": step_s * 1e6, "state_GBps": gbs,
                             "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
                             "alg_bytes_per_step": decode_bytes(wd.N, wd.H, wd.dk),
-                            "traffic": profiled_traffic("kda_decode_kernel_n256.md",
-                                                        ["kda_decode.hip", "kda_device.h"]),
+                            "traffic": profiled_value("kda_decode_kernel_n256.md",
+                                                      ["kda_decode.hip", "kda_device.h"]),
                             "tokens_per_s": wd.N * args.decode_steps / dwall}
     if not args.prefill_only and not args.no_spec:
         result["spec_decode"] = bench_spec(kda, gen)

@@ -57,7 +57,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_library_has_no_undefined_own_symbols():
     """Every kernel launch stub and internal symbol of libkda is defined in the library
-    itself (a missing one would only surface when the library is loaded on a GPU machine)."""
+    itself (a missing one would only surface when the library is loaded on a machine with a GPU)."""
     out = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     own = [line for line in out.splitlines() if "kda" in line]
