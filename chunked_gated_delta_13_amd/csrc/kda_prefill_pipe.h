@@ -487,6 +487,26 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
     for (int i = 0; i < 4; ++i) barrier_lds();
 }
 
+// Operand sequence of the state waves' output product: for each row tile ar, the NKB blocks of
+// Q~ (bqk = false, kb = block), then the blocks kb = 0 .. ar/2 of Bqk (bqk = true).
+struct PipeOStep {
+    int ar, kb;
+    bool bqk;
+};
+constexpr PipeOStep pipe_o_step(int i, int nt, int nkb) {
+    for (int ar = 0; ar < nt; ++ar) {
+        const int n = nkb + ar / 2 + 1;
+        if (i < n) return PipeOStep{ar, i < nkb ? i : i - nkb, i >= nkb};
+        i -= n;
+    }
+    return PipeOStep{-1, 0, false};
+}
+constexpr int pipe_o_steps(int nt, int nkb) {
+    int n = 0;
+    for (int ar = 0; ar < nt; ++ar) n += nkb + ar / 2 + 1;
+    return n;
+}
+
 // State waves (NCW .. NCW+3): state wave sw holds state columns 32 sw .. 32 sw + 31 in
 // fp32 registers and runs the state-dependent products of each chunk.  Four barriers while the
 // chunk waves prepare the first chunk, then four per chunk.
@@ -568,16 +588,24 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
         for (int ar = 0; ar < NT; ++ar)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = zero4();
+        // K~ fragments one contraction block ahead: the loads of block kb + 1 are issued before
+        // the products of block kb, so their LDS latency overlaps the matrix-core work
+        Frag<OpT> fk[2][NT];
+#pragma unroll
+        for (int ar = 0; ar < NT; ++ar) frag_ld(fk[0][ar], pQs + eKt + 16 * ar * PK);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            Frag<OpT> fk[NT], fs[NCT];
+            if (kb + 1 < NKB) {
 #pragma unroll
-            for (int ar = 0; ar < NT; ++ar) frag_ld(fk[ar], pQs + eKt + 16 * ar * PK + 32 * kb);
+                for (int ar = 0; ar < NT; ++ar) frag_ld(fk[(kb + 1) & 1][ar], pQs + eKt + 16 * ar * PK + 32 * (kb + 1));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            Frag<OpT> fs[NCT];
             s_frag(fs, kb);
 #pragma unroll
             for (int ar = 0; ar < NT; ++ar)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = mma(fk[ar], fs[ct], Rh[ar][ct]);
+                for (int ct = 0; ct < NCT; ++ct) Rh[ar][ct] = mma(fk[kb & 1][ar], fs[ct], Rh[ar][ct]);
         }
 #pragma unroll
         for (int ar = 0; ar < NT; ++ar) {
@@ -602,21 +630,34 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
         // ---- interval 1: U_a = T_aa (RHS_a - sum_{b<a} A_ab U_b) ----
         f32x4_t U[NT][NCT];
         Frag<OpT> fU[NTB][NCT];
+        // every T/A fragment of the solve is requested up front (they were written in the previous
+        // interval 4), so the chain of dependent products below waits on LDS at most once
+        static_assert(NT == 4, "fragment list of the blocked solve");
+        Frag<OpT> fsol[8];   // T00 | A10, T11 | A2(0..31), T22 | A3(0..31), A32, T33
+        frag_ld_lo(fsol[0], pTs);
+        frag_ld_lo(fsol[1], pTs + 16 * PTB);
+        frag_ld_lo(fsol[2], pTs + 16 * PTB + 16);
+        frag_ld(fsol[3], pTs + 32 * PTB);
+        frag_ld_lo(fsol[4], pTs + 32 * PTB + 32);
+        frag_ld(fsol[5], pTs + 48 * PTB);
+        frag_ld_lo(fsol[6], pTs + 48 * PTB + 32);
+        frag_ld_lo(fsol[7], pTs + 48 * PTB + 48);
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int sol_first[NT] = {0, 1, 3, 5};
 #pragma unroll
         for (int ar = 0; ar < NT; ++ar) {
+            int fi = sol_first[ar];
             f32x4_t W[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) W[ct] = Rh[ar][ct];
 #pragma unroll
             for (int kb = 0; kb < ar / 2; ++kb) {
-                Frag<OpT> fa;
-                frag_ld(fa, pTs + 16 * ar * PTB + 32 * kb);
+                const Frag<OpT>& fa = fsol[fi++];
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) W[ct] = mma(fa, fU[kb][ct], W[ct]);
             }
             if (ar & 1) {
-                Frag<OpT> fa;
-                frag_ld_lo(fa, pTs + 16 * ar * PTB + 16 * (ar - 1));
+                const Frag<OpT>& fa = fsol[fi++];
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     Frag<OpT> fb;
@@ -624,8 +665,7 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
                     W[ct] = mma(fa, fb, W[ct]);
                 }
             }
-            Frag<OpT> ft;
-            frag_ld_lo(ft, pTs + 16 * ar * PTB + 16 * ar);
+            const Frag<OpT>& ft = fsol[fi];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 Frag<OpT> fw;
@@ -640,43 +680,49 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
         barrier_lds();
 
         // ---- interval 2: O^T = S^T Q~^T + U^T Bqk^T, stored from the accumulators ----
+        // One row tile at a time: its four Q~ blocks, then its Bqk blocks kb = 0 .. ar/2, with the
+        // operand fragments loaded OLA steps ahead of their products (a rolling buffer), so the
+        // LDS latency overlaps the matrix-core work.  The accumulation order per output element is
+        // the same as block by block over all row tiles.
         if (go) {
-            f32x4_t Oa[NT][NCT];
+            Frag<OpT> fsa[NKB][NCT];   // S as the A operand, all 128 rows
 #pragma unroll
-            for (int ar = 0; ar < NT; ++ar)
+            for (int kb = 0; kb < NKB; ++kb) s_frag(fsa[kb], kb);
+            constexpr int NS = pipe_o_steps(NT, NKB);
+            constexpr int OLA = 3;
+            Frag<OpT> fb[OLA + 1];
+            auto o_load = [&](auto Ic) {
+                constexpr int i = decltype(Ic)::value;
+                constexpr PipeOStep st_i = pipe_o_step(i, NT, NKB);
+                if constexpr (st_i.bqk) frag_ld(fb[i % (OLA + 1)], pTs + eBs + 16 * st_i.ar * PTB + 32 * st_i.kb);
+                else frag_ld(fb[i % (OLA + 1)], pQs + 16 * st_i.ar * PK + 32 * st_i.kb);
+            };
+            static_for<0, OLA>([&](auto Ic) { o_load(Ic); });
+            f32x4_t O[NCT];
+            static_for<0, NS>([&](auto Ic) {
+                constexpr int i = decltype(Ic)::value;
+                constexpr PipeOStep st_i = pipe_o_step(i, NT, NKB);
+                constexpr int ar = st_i.ar;
+                if constexpr (i + OLA < NS) o_load(std::integral_constant<int, i + OLA>{});
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (!st_i.bqk && st_i.kb == 0) {
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) Oa[ar][ct] = zero4();
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                Frag<OpT> fq[NT], fs[NCT];
-#pragma unroll
-                for (int ar = 0; ar < NT; ++ar) frag_ld(fq[ar], pQs + 16 * ar * PK + 32 * kb);
-                s_frag(fs, kb);
-#pragma unroll
-                for (int ar = 0; ar < NT; ++ar)
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) Oa[ar][ct] = mma(fs[ct], fq[ar], Oa[ar][ct]);
-            }
-#pragma unroll
-            for (int ar = 0; ar < NT; ++ar) {
-                f32x4_t O[NCT];
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) O[ct] = Oa[ar][ct];
-#pragma unroll
-                for (int kb = 0; kb <= ar / 2; ++kb) {
-                    Frag<OpT> fb;
-                    frag_ld(fb, pTs + eBs + 16 * ar * PTB + 32 * kb);
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) O[ct] = mma(fU[kb][ct], fb, O[ct]);
+                    for (int ct = 0; ct < NCT; ++ct) O[ct] = zero4();
                 }
-                if (c0 + 16 * ar + lr < t_end) {
-                    TIn* const orow = go + (c0 + 16 * ar) * HD;
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-                        *reinterpret_cast<u32x2_t*>(at_byte(orow, pinned_u(boO + 32 * ct))) =
-                            Quad<TIn>::pack(O[ct][0], O[ct][1], O[ct][2], O[ct][3]);
+                for (int ct = 0; ct < NCT; ++ct)
+                    O[ct] = st_i.bqk ? mma(fU[st_i.kb][ct], fb[i % (OLA + 1)], O[ct])
+                                     : mma(fsa[st_i.kb][ct], fb[i % (OLA + 1)], O[ct]);
+                if constexpr (st_i.bqk && st_i.kb == ar / 2) {
+                    if (c0 + 16 * ar + lr < t_end) {
+                        TIn* const orow = go + (c0 + 16 * ar) * HD;
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+                            *reinterpret_cast<u32x2_t*>(at_byte(orow, pinned_u(boO + 32 * ct))) =
+                                Quad<TIn>::pack(O[ct][0], O[ct][1], O[ct][2], O[ct][3]);
+                    }
                 }
-            }
+            });
         }
         barrier_lds();
 
