@@ -163,26 +163,32 @@ def bench_prefill_gate(kda, gen, w, d, steps, warmup):
 
 
 def bench_long(kda, gen, steps, warmup):
+    """The 1M-token prefill with the workload's 64K-token segments, then with the library's own
+    plan (segment 0 longer, run beside the transition/increment pass of the middle segments)."""
     import torch
     w = gen.WORKLOADS["long_1m"]
     log(f"[long] generating {w.note} on the device")
     d = gen.workload_inputs(w, device="cuda")
     o = torch.empty_like(d["v"])
     st = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
-    need = kda.prefill_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.chunk, seg_len=w.segment)
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    res = []
+    for seg in (w.segment, 0):
+        need = kda.prefill_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.chunk, seg_len=seg)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
 
-    def step():
-        kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
-                          chunk=w.chunk, seg_len=w.segment, o=o, S_T=st, workspace=ws)
+        def step():
+            kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
+                              chunk=w.chunk, seg_len=seg, o=o, S_T=st, workspace=ws)
 
-    wall, ev = time_loop(step, steps, warmup, stream)
-    assert torch.isfinite(st).all()
-    log(f"[long] {steps} steps: wall {wall*1e3:.2f} ms, events {ev*1e3:.2f} ms")
-    del d, o, ws
+        wall, ev = time_loop(step, steps, warmup, stream)
+        assert torch.isfinite(st).all()
+        log(f"[long] seg_len {seg}: {steps} steps: wall {wall*1e3:.2f} ms, events {ev*1e3:.2f} ms")
+        res.append((wall, ev))
+        del ws
+    del d, o
     torch.cuda.empty_cache()
-    return w, wall, ev
+    return w, res
 
 
 def bench_decode(kda, gen, steps=1000, pool=8):
@@ -420,11 +426,16 @@ def main():
     if not args.prefill_only and not args.no_spec:
         result["spec_decode"] = bench_spec(kda, gen)
     if not args.prefill_only and not args.no_long:
-        wl, lwall, lev = bench_long(kda, gen, max(2, args.steps // 5), 1)
         nsteps = max(2, args.steps // 5)
+        wl, lres = bench_long(kda, gen, nsteps, 1)
+        (lwall, _), (awall, _) = lres
+        auto_seg, _ = kda.prefill_plan(wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.chunk)
         result["long_context"] = {"workload": wl.note, "seg_len": wl.segment, "steps": nsteps,
                                   "ms_per_step": lwall / nsteps * 1e3,
-                                  "tokens_per_s": wl.B * wl.T * nsteps / lwall}
+                                  "tokens_per_s": wl.B * wl.T * nsteps / lwall,
+                                  "automatic_plan": {"seg_len_after_first": auto_seg,
+                                                     "ms_per_step": awall / nsteps * 1e3,
+                                                     "tokens_per_s": wl.B * wl.T * nsteps / awall}}
     print(json.dumps(result), flush=True)
 
 

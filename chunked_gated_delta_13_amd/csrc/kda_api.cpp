@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/kda.h"
@@ -44,6 +46,39 @@ bool mul_ok(long long a, long long b, long long* out) {
     if (a != 0 && b > (1LL << 62) / a) return false;
     *out = a * b;
     return true;
+}
+
+// A second stream per device for work that overlaps the caller's stream (created once, default
+// priority, never destroyed), with the two events that fork it from and join it back to the
+// caller's stream.  Callers hold g_side_mu while they enqueue a fork ... join sequence.
+struct SideStream {
+    hipStream_t stream;
+    hipEvent_t fork, join;
+};
+std::mutex g_side_mu;
+SideStream* side_stream() {
+    static SideStream side[64];
+    static bool made[64] = {false};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (!made[dev]) {
+        SideStream x;
+        if (hipStreamCreateWithFlags(&x.stream, hipStreamNonBlocking) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        if (hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        side[dev] = x;
+        made[dev] = true;
+    }
+    return &side[dev];
 }
 
 int cu_count() {
@@ -125,9 +160,28 @@ int spec_chunk(int m, kda_dtype_t dt) {
     return 64;
 }
 
-// The automatic plan: column slices first (no extra work beyond the shared
-// per-chunk tiles), then segments when even that leaves most compute units idle.
-void auto_plan(int B, int T, int H, int dk, int dv, int chunk, bool f32, int* seg_len, int* n_vs) {
+// Per-chunk cost of the transition/increment work relative to an output pass at the same shape,
+// measured on the MI355X at d = 128: the shared pass of 8-wave shapes 6.9 us against 5.2 us per
+// 64-token chunk; 4-wave shapes run two separate passes.
+constexpr double kSharedPassCost = 1.3;
+constexpr double kTwoPassCost = 2.0;
+
+// Segments of a split: segment 0 holds seg_len + shift tokens, every later one seg_len (the last
+// one possibly fewer).
+long long segment_count(long long T, long long seg_len, long long shift) {
+    if (T <= seg_len + shift) return 1;
+    return 1 + (T - seg_len - shift + seg_len - 1) / seg_len;
+}
+
+// The automatic plan: column slices first (no extra work beyond the shared per-chunk tiles),
+// then segments when even that leaves most compute units idle.  A split runs in two phases of
+// units * (n - 1) workgroups each, one per compute unit: first segment 0 from S0 with its outputs
+// beside the transitions and increments of segments 1 .. n-2, then segments 1 .. n-1 from their
+// entry states.  A phase never takes every compute unit (on the MI355X, phases that needed all
+// 256 at once ran up to 13% slower at times).  Segment 0 is longer than the others by the cost
+// ratio of the two kinds of pass, so that both halves of the first phase end together.
+void auto_plan(int B, int T, int H, int dk, int dv, int chunk, bool f32, int* seg_len, int* n_vs,
+               long long* shift) {
     const long long cus = cu_count();
     const long long bh = (long long)B * H;
     // Two column slices only pay where a 128-column workgroup has 4 waves (32 columns each):
@@ -136,36 +190,54 @@ void auto_plan(int B, int T, int H, int dk, int dv, int chunk, bool f32, int* se
     // intra-chunk work; the sequence split below is what shortens the chain of chunks.
     const bool eight = kda::prefill_waves(dk, dv, f32) == 8;
     int vs = (dv == 128 && !eight && 2 * bh <= cus) ? 2 : 1;
-    long long seg = T;
+    long long seg = T, sh = 0;
     const long long units = bh * vs;
-    if (units > 0 && 2 * units <= cus && (long long)T >= 2 * kMinSegTokens) {
-        long long nseg = cus / units;
-        if (nseg > T / kMinSegTokens) nseg = T / kMinSegTokens;
-        if (nseg >= 2) {
-            seg = ((long long)T + nseg - 1) / nseg;
-            seg = (seg + chunk - 1) / chunk * chunk;
+    if (units > 0 && 2 * units <= cus && (long long)T >= 3 * kMinSegTokens) {
+        long long m = (cus - 1) / units;   // segments after the first
+        if (m > T / kMinSegTokens - 1) m = T / kMinSegTokens - 1;
+        if (const char* e = getenv("KDA_SPLIT_MAX")) {   // tuning only: cap on m
+            const long long v = atoll(e);
+            if (v >= 2 && v < m) m = v;
+        }
+        if (m >= 2) {
+            const double r = kda::prefill_dual_supported(dk, dv / vs, chunk, f32) ? kSharedPassCost : kTwoPassCost;
+            long long L = (long long)((double)T / (r + (double)m)) + 1;
+            L = (L + chunk - 1) / chunk * chunk;
+            long long rest = (long long)T - (m + 1) * L;
+            if (rest < 0) rest = 0;
+            sh = (rest + chunk - 1) / chunk * chunk;
+            seg = L;
         }
     }
     if (seg_len) *seg_len = (int)(seg > 0 ? seg : chunk);
     if (n_vs) *n_vs = vs;
+    if (shift) *shift = seg > 0 && seg < T ? sh : 0;
 }
 
-// Resolve an explicit or automatic plan.  n_seg == 1 means no split.
+// Resolve an explicit or automatic plan.  n_seg == 1 means no split.  An explicit seg_len gives
+// segments of equal length (shift 0).
 kda_status_t resolve_plan(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt,
-                          int seg_len_in, int n_vs_in, long long* seg_len, int* n_seg, int* n_vs) {
+                          int seg_len_in, int n_vs_in, long long* seg_len, int* n_seg, int* n_vs,
+                          long long* shift) {
     int a_seg = 0, a_vs = 0;
-    auto_plan(B, T, H, dk, dv, chunk, dt == KDA_F32, &a_seg, &a_vs);
+    long long a_sh = 0;
+    auto_plan(B, T, H, dk, dv, chunk, dt == KDA_F32, &a_seg, &a_vs, &a_sh);
     long long sl = seg_len_in > 0 ? seg_len_in : a_seg;
+    long long sh = seg_len_in > 0 ? 0 : a_sh;
     if (seg_len_in < 0 || (seg_len_in > 0 && seg_len_in % chunk != 0)) return KDA_ERR_INVALID_ARGUMENT;
     int vs = n_vs_in > 0 ? n_vs_in : a_vs;
     if (n_vs_in < 0 || vs > 2 || (vs == 2 && dv != 128)) return KDA_ERR_INVALID_ARGUMENT;
     if (!kda::prefill_supported(dk, dv / vs, chunk, dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
-    if (sl <= 0 || sl >= T) sl = T > 0 ? T : chunk;
-    long long ns = T > 0 ? ((long long)T + sl - 1) / sl : 1;
+    if (sl <= 0 || sl + sh >= T) {
+        sl = T > 0 ? T : chunk;
+        sh = 0;
+    }
+    const long long ns = T > 0 ? segment_count(T, sl, sh) : 1;
     if (ns > (1 << 20)) return KDA_ERR_UNSUPPORTED;
     *seg_len = sl;
     *n_seg = (int)ns;
     *n_vs = vs;
+    if (shift) *shift = sh;
     return KDA_OK;
 }
 
@@ -264,7 +336,7 @@ kda_status_t kda_chunk_prefill_plan(int B, int T, int H, int dk, int dv, int chu
     if (st != KDA_OK) return st;
     long long sl = 0;
     int ns = 0, vs = 0;
-    const kda_status_t st2 = resolve_plan(B, T, H, dk, dv, chunk, dt, 0, 0, &sl, &ns, &vs);
+    const kda_status_t st2 = resolve_plan(B, T, H, dk, dv, chunk, dt, 0, 0, &sl, &ns, &vs, nullptr);
     if (st2 != KDA_OK) return st2;
     if (seg_len) *seg_len = (int)sl;
     if (n_vs) *n_vs = vs;
@@ -276,7 +348,7 @@ size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, in
     if (check_prefill_shape(B, T, H, dk, dv, chunk, dt) != KDA_OK) return 0;
     long long sl = 0;
     int ns = 0, vs = 0;
-    if (resolve_plan(B, T, H, dk, dv, chunk, dt, seg_len, 0, &sl, &ns, &vs) != KDA_OK) return 0;
+    if (resolve_plan(B, T, H, dk, dv, chunk, dt, seg_len, 0, &sl, &ns, &vs, nullptr) != KDA_OK) return 0;
     return workspace_for(B, H, dk, dv, ns);
 }
 
@@ -324,9 +396,9 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     const size_t decay_esz = gmode ? 2 : sizeof(float);
     if (ckpt_every < 0 || (ckpt_every > 0 && ckpt_every % chunk != 0)) return KDA_ERR_INVALID_ARGUMENT;
     const int n_ckpt = ckpt_every > 0 ? T / ckpt_every : 0;
-    long long sl = 0;
+    long long sl = 0, shift = 0;
     int ns = 0, vs = 0;
-    st = resolve_plan(B, T, H, dk, dv, chunk, dt, seg_len, n_vs, &sl, &ns, &vs);
+    st = resolve_plan(B, T, H, dk, dv, chunk, dt, seg_len, n_vs, &sl, &ns, &vs, &shift);
     if (st != KDA_OK) return st;
     if (B == 0 || H == 0) return KDA_OK;
 
@@ -428,14 +500,39 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
         return KDA_OK;
     }
 
-    // ---- sequence split: transitions and increments, scan, then every segment ----
+    // ---- sequence split ----
+    // Phase 1: segment 0 runs from S0 with its outputs (on a side stream) while the transitions
+    // M_s and increments H_s of segments 1 .. ns-2 are formed (on the caller's stream); segment 0's
+    // final state is the entry state S_in(1).  Then the scan S_in(s+1) = M_s S_in(s) + H_s for
+    // s = 1 .. ns-2, and phase 2 runs segments 1 .. ns-1 from their entry states with outputs.
     float* ws = reinterpret_cast<float*>(workspace);
     const long long bh = (long long)B * H;
     float* wsM = ws;
     float* wsH = wsM + bh * (ns - 1) * SS;
     float* wsSin = wsH + bh * (ns - 1) * SS;
+    a.seg_shift = shift;
 
-    PrefillArgs pm = a;  // M_s: identity columns, zero values, no output
+    PrefillArgs p0 = a;  // segment 0 from S0, with outputs and checkpoints; final state -> S_in(1)
+    p0.o = o;
+    p0.s_in = S0;
+    p0.sin_bh_stride = SS;
+    p0.sin_seg_stride = 0;
+    p0.init_mode = S0 ? 1 : 0;
+    p0.s_out = wsSin + SS;
+    p0.sout_bh_stride = (long long)ns * SS;
+    p0.sout_seg_stride = 0;
+    p0.out_seg = 0;
+    p0.seg0 = 0;
+    p0.n_seg_launch = 1;
+    p0.n_units = (int)bh;
+    p0.zero_values = 0;
+    if (n_ckpt > 0) {   // the passes that run from true entry states write the checkpoints
+        p0.s_ckpt = S_ckpt;
+        p0.ckpt_every = ckpt_every;
+        p0.n_ckpt = n_ckpt;
+    }
+
+    PrefillArgs pm = a;  // M_s: identity columns, zero values, no output (segments 1 .. ns-2)
     pm.o = nullptr;
     pm.s_in = nullptr;
     pm.init_mode = 2;
@@ -444,9 +541,9 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     pm.sout_bh_stride = (long long)(ns - 1) * SS;
     pm.sout_seg_stride = SS;
     pm.out_seg = -1;
-    pm.seg0 = 0;
-    pm.n_seg_launch = ns - 1;
-    pm.n_units = (int)(bh * (ns - 1));
+    pm.seg0 = 1;
+    pm.n_seg_launch = ns - 2;
+    pm.n_units = (int)(bh * (ns - 2));
     // The shared transition/increment pass may use another chunk than the output pass (M_s and
     // H_s do not depend on it beyond rounding).  It uses the caller's chunk: at 64 tokens the two
     // states spill a few registers outside the chunk loop, and the pass is still faster than at
@@ -454,36 +551,57 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     int dchunk = chunk > kDualChunk ? kDualChunk : chunk;
     if (const char* e = getenv("KDA_DUAL_CHUNK")) {
         const int v = atoi(e);
-        if ((v == 16 || v == 32 || v == 64) && sl % v == 0) dchunk = v;
+        if ((v == 16 || v == 32 || v == 64) && sl % v == 0 && shift % v == 0) dchunk = v;
     }
-    if (kda::prefill_dual_supported(dk, dvw, dchunk, f32)) {
-        PrefillArgs pd = pm;  // M_s and H_s together: the decay and intra-chunk work is shared
-        pd.init_mode = 0;
-        pd.zero_values = 0;
-        pd.s_out = wsH;
-        pd.s_aux = wsM;
-        pd.saux_bh_stride = pm.sout_bh_stride;
-        pd.saux_seg_stride = pm.sout_seg_stride;
-        if (kda::launch_prefill_dual(dk, dvw, dchunk, f32, pd, s) != hipSuccess) return KDA_ERR_DEVICE;
-    } else {
-        if (kda::launch_prefill(dk, dvw, chunk, f32, pm, s) != hipSuccess) return KDA_ERR_DEVICE;
-        PrefillArgs ph = pm;  // H_s: zero start, real values, no output
-        ph.init_mode = 0;
-        ph.zero_values = 0;
-        ph.s_out = wsH;
-        if (kda::launch_prefill(dk, dvw, chunk, f32, ph, s) != hipSuccess) return KDA_ERR_DEVICE;
+
+    {
+        // segment 0 overlaps the transition/increment pass on a side stream: fork after the
+        // caller's earlier work, join before the scan.  One host thread at a time per library, so
+        // the shared fork/join events are recorded and waited in order.
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        SideStream* side = ns > 2 ? side_stream() : nullptr;
+        hipStream_t s0s = side ? side->stream : s;
+        if (side) {
+            if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
+                return KDA_ERR_DEVICE;
+        }
+        if (kda::launch_prefill(dk, dvw, chunk, f32, p0, s0s) != hipSuccess) return KDA_ERR_DEVICE;
+        if (ns > 2) {
+            if (kda::prefill_dual_supported(dk, dvw, dchunk, f32)) {
+                PrefillArgs pd = pm;  // M_s and H_s together: the decay and intra-chunk work is shared
+                pd.init_mode = 0;
+                pd.zero_values = 0;
+                pd.s_out = wsH;
+                pd.s_aux = wsM;
+                pd.saux_bh_stride = pm.sout_bh_stride;
+                pd.saux_seg_stride = pm.sout_seg_stride;
+                if (kda::launch_prefill_dual(dk, dvw, dchunk, f32, pd, s) != hipSuccess) return KDA_ERR_DEVICE;
+            } else {
+                if (kda::launch_prefill(dk, dvw, chunk, f32, pm, s) != hipSuccess) return KDA_ERR_DEVICE;
+                PrefillArgs ph = pm;  // H_s: zero start, real values, no output
+                ph.init_mode = 0;
+                ph.zero_values = 0;
+                ph.s_out = wsH;
+                if (kda::launch_prefill(dk, dvw, chunk, f32, ph, s) != hipSuccess) return KDA_ERR_DEVICE;
+            }
+        }
+        if (side) {
+            if (hipEventRecord(side->join, side->stream) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
+                return KDA_ERR_DEVICE;
+        }
     }
 
     kda::ScanArgs sa;
     sa.M = wsM;
     sa.Hinc = wsH;
     sa.S0 = S0;
-    sa.S_in = wsSin;  // S0 is copied here first, so S_T may alias S0
+    sa.S_in = wsSin;
     sa.BH = (int)bh;
     sa.n_seg = ns;
-    if (kda::launch_scan(dk, sa, s) != hipSuccess) return KDA_ERR_DEVICE;
+    sa.s_first = 1;   // S_in(1) was written by segment 0's pass
+    if (ns > 2 && kda::launch_scan(dk, sa, s) != hipSuccess) return KDA_ERR_DEVICE;
 
-    PrefillArgs pf = a;  // every segment from its entry state, with outputs
+    PrefillArgs pf = a;  // segments 1 .. ns-1 from their entry states, with outputs
     pf.o = o;
     pf.s_in = wsSin;
     pf.sin_bh_stride = (long long)ns * SS;
@@ -494,10 +612,10 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     pf.sout_bh_stride = SS;
     pf.sout_seg_stride = 0;
     pf.out_seg = ns - 1;
-    pf.seg0 = 0;
-    pf.n_seg_launch = ns;
-    pf.n_units = (int)(bh * ns);
-    if (n_ckpt > 0) {   // only the pass that runs from the true entry states writes checkpoints
+    pf.seg0 = 1;
+    pf.n_seg_launch = ns - 1;
+    pf.n_units = (int)(bh * (ns - 1));
+    if (n_ckpt > 0) {
         pf.s_ckpt = S_ckpt;
         pf.ckpt_every = ckpt_every;
         pf.n_ckpt = n_ckpt;
@@ -582,7 +700,7 @@ kda_status_t kda_spec_commit(const void* q, const void* k, const void* v, const 
     if (st != KDA_OK) return st;
     long long sl = 0;
     int ns = 0, vs = 0;
-    st = resolve_plan(N, m, H, dk, dv, chunk, dt, 0, 0, &sl, &ns, &vs);
+    st = resolve_plan(N, m, H, dk, dv, chunk, dt, 0, 0, &sl, &ns, &vs, nullptr);
     if (st != KDA_OK) return st;
     if (ns != 1) return KDA_ERR_UNSUPPORTED;
     if (N == 0 || H == 0) return KDA_OK;

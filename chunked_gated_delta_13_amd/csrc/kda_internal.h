@@ -30,6 +30,7 @@ struct PrefillArgs {
     long long T;              // tokens per sequence
     int B, H;
     long long seg_len;        // tokens per segment
+    long long seg_shift;      // extra tokens of segment 0: segment s >= 1 starts at s * seg_len + seg_shift
     int seg0;                 // first segment index of this launch
     int n_seg_launch;         // segments per (b, h) in this launch
     int n_vs;                 // state-column slices per unit
@@ -57,9 +58,10 @@ struct ScanArgs {
     const float* M;           // [B*H, n_seg-1, DK, DK]
     const float* Hinc;        // [B*H, n_seg-1, DK, DK]
     const float* S0;          // [B*H, DK, DK] or nullptr
-    float* S_in;              // [B*H, n_seg, DK, DK]  (out)
+    float* S_in;              // [B*H, n_seg, DK, DK]  (out; with s_first = 1, S_in(1) is an input)
     int BH;
     int n_seg;
+    int s_first;              // 0: start from S0; 1: start from S_in(1), already in place
 };
 
 // Decode step (m = 1) or a block of m <= kDecodeMaxTokens tokens per (sequence, head) run from

@@ -204,8 +204,9 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     const int h = bh % a.H;
     const int b = bh / a.H;
     const int s = a.seg0 + sl;
-    const long long t_begin = (long long)s * a.seg_len;
-    long long t_end = (t_begin + a.seg_len < a.T) ? t_begin + a.seg_len : a.T;
+    const long long t_begin = (long long)s * a.seg_len + (s > 0 ? a.seg_shift : 0);
+    const long long t_next = (long long)(s + 1) * a.seg_len + a.seg_shift;
+    long long t_end = t_next < a.T ? t_next : a.T;
     if (a.lens) {   // ragged: this sequence stops after lens[b] tokens
         const long long l = a.lens[b];
         const long long lc = l < 0 ? 0 : (l > a.T ? a.T : l);

@@ -796,8 +796,9 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void kda_prefill_pipe_kernel(const 
     u.h = u.bh % a.H;
     u.b = u.bh / a.H;
     u.s = a.seg0 + sl;
-    u.t_begin = (long long)u.s * a.seg_len;
-    u.t_end = (u.t_begin + a.seg_len < a.T) ? u.t_begin + a.seg_len : a.T;
+    u.t_begin = (long long)u.s * a.seg_len + (u.s > 0 ? a.seg_shift : 0);
+    const long long t_next = (long long)(u.s + 1) * a.seg_len + a.seg_shift;
+    u.t_end = t_next < a.T ? t_next : a.T;
     const long long ntok = u.t_end - u.t_begin;
     u.nchunks = ntok > 0 ? (int)((ntok + C - 1) / C) : 0;
     u.HD = (long long)a.H * DK;

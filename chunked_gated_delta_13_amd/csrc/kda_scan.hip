@@ -7,7 +7,8 @@
 // comes due in the serving stack" (the per-segment transition and the state
 // reached from zero combine exactly across segments).
 //
-// Entry state of segment s:  S_in(0) = S0,  S_in(s+1) = M_s S_in(s) + H_s.
+// Entry state of segment s:  S_in(0) = S0,  S_in(s+1) = M_s S_in(s) + H_s.  With s_first = 1 the
+// walk starts from S_in(1), already written by the pass that ran segment 0 from S0.
 // State columns are independent, so a workgroup owns (head, 16 columns) and
 // keeps that column block of S_in in LDS while it walks the segments.  fp32
 // throughout; the n_seg - 1 steps are tiny next to the chunk passes around them.
@@ -32,14 +33,19 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(const ScanArgs a) {
 
     __shared__ float sS[DK][CB + 1];
     float cur[CPT];
-    const float* s0 = a.S0 ? a.S0 + bh * SS : nullptr;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) cur[j] = s0 ? s0[(long long)row * DK + c0 + j] : 0.0f;
     float* sin = a.S_in + (long long)bh * a.n_seg * SS;
+    if (a.s_first == 0) {
+        const float* s0 = a.S0 ? a.S0 + bh * SS : nullptr;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) sin[(long long)row * DK + c0 + j] = cur[j];
+        for (int j = 0; j < CPT; ++j) cur[j] = s0 ? s0[(long long)row * DK + c0 + j] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) sin[(long long)row * DK + c0 + j] = cur[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) cur[j] = sin[(long long)a.s_first * SS + (long long)row * DK + c0 + j];
+    }
 
-    for (int s = 0; s + 1 < a.n_seg; ++s) {
+    for (int s = a.s_first; s + 1 < a.n_seg; ++s) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < CPT; ++j) sS[row][c0 - cb * CB + j] = cur[j];
@@ -72,6 +78,7 @@ __global__ __launch_bounds__(256) void kda_state_copy_kernel(float* dst, const f
 
 hipError_t launch_scan(int dk, const ScanArgs& a, hipStream_t stream) {
     if (a.BH <= 0 || a.n_seg <= 0) return hipSuccess;
+    if (a.s_first < 0 || a.s_first >= a.n_seg) return hipErrorInvalidValue;
     const long long nblk = (long long)a.BH * (dk / 16);
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (dk == 128) hipLaunchKernelGGL(kda_scan_kernel<128>, dim3((unsigned)nblk), dim3(256), 0, stream, a);

@@ -65,10 +65,13 @@ const char *kda_status_string(kda_status_t status);
 
 /*
  * Sequence-split plan that kda_chunk_prefill picks for a shape (the automatic
- * scheduler): `seg_len` tokens per segment (== T when the sequence is not
- * split) and `n_vs` state-column slices per head.  Pages: "Kimi K3",
- * "Parallelizing Sequential State Updates" (a scheduler spreads long-context
- * prefill over the compute units of one card).  Any output pointer may be NULL.
+ * scheduler): `seg_len` tokens per segment after the first (== T when the
+ * sequence is not split; the first segment holds the remaining tokens and is
+ * the longest, since it runs from S0 while the transitions of the middle
+ * segments are formed) and `n_vs` state-column slices per head.  Pages: "Kimi
+ * K3", "Parallelizing Sequential State Updates" (a scheduler spreads
+ * long-context prefill over the compute units of one card).  Any output
+ * pointer may be NULL.
  */
 kda_status_t kda_chunk_prefill_plan(int B, int T, int H, int dk, int dv, int chunk,
                                     kda_dtype_t dtype, int *seg_len, int *n_vs);
@@ -113,14 +116,21 @@ kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v,
 
 /*
  * kda_chunk_prefill with an explicit plan: `seg_len` tokens per segment (a
- * positive multiple of `chunk`; 0 = automatic; >= T = no split) and `n_vs`
- * state-column slices (1 or 2 for dv = 128, 1 for dv = 64; 0 = automatic).
- * With a split, each segment's transition M_s (the recurrence applied to the
- * identity with zero values) and increment H_s (from a zero state) are formed
- * first, joined by an on-device prefix scan S_in(s+1) = M_s S_in(s) + H_s, and
- * every segment is then run from its entry state.  Pages: "Kimi K3's
- * architecture", "The bill comes due in the serving stack" (per segment, the transition and
- * the state reached from zero combine exactly across segments).
+ * positive multiple of `chunk`, all segments equal but the last; 0 = automatic;
+ * >= T = no split) and `n_vs` state-column slices (1 or 2 for dv = 128, 1 for
+ * dv = 64; 0 = automatic).  With a split, segment 0 runs from S0 with its
+ * outputs while the transitions M_s (the recurrence applied to the identity
+ * with zero values) and increments H_s (from a zero state) of segments
+ * 1 .. n-2 are formed; an on-device prefix scan S_in(s+1) = M_s S_in(s) + H_s
+ * from segment 0's final state gives every later entry state, and segments
+ * 1 .. n-1 then run from them.  Segment 0 runs on a second stream of the
+ * library (created once per device, default priority) joined back to `stream`
+ * by events (fork after the work already on `stream`, join before the scan); the
+ * call stays asynchronous.  Calls from several host threads are serialised
+ * while they enqueue a split.
+ * Pages: "Kimi K3's architecture", "The bill comes due in the serving stack"
+ * (per segment, the transition and the state reached from zero combine
+ * exactly across segments).
  * The workspace must hold kda_chunk_prefill_workspace_bytes(..., seg_len).
  */
 kda_status_t kda_chunk_prefill_ex(const void *q, const void *k, const void *v,

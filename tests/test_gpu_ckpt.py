@@ -27,6 +27,7 @@ def _kda():
     ("bf16", 64, 640, 32, 64, 0),
     ("f32", 64, 300, 16, 32, 0),
     ("bf16", 128, 512, 64, 512, 0),        # one checkpoint, at the last token
+    ("bf16", 128, 12288, 64, 4096, 0),     # automatic split: segments 4480 + 3904 + 3904 tokens
 ])
 def test_prefill_checkpoints_match_oracle(dtype, d, T, chunk, every, seg):
     kda = _kda()

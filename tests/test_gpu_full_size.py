@@ -70,6 +70,20 @@ def test_long_context_split_prefill_sampled_head():
     assert torch.equal(st, st2) and torch.equal(o[:, -4096:], o2[:, -4096:])
 
 
+def test_long_context_automatic_plan_sampled_head():
+    """The same workload on the library's own plan: 17 segments, the first one longer, run
+    from S0 beside the transition/increment pass of the middle segments."""
+    kda = _kda()
+    w = gen.WORKLOADS["long_1m"]
+    seg, _ = kda.prefill_plan(w.B, w.T, w.H, w.dk, w.dv, w.chunk)
+    print(f"long context, automatic plan: segments of {seg} tokens after the first", flush=True)
+    d = gen.workload_inputs(w, device="cuda")
+    o, st = kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"], chunk=w.chunk)
+    torch.cuda.synchronize()
+    assert torch.isfinite(st).all()
+    _check_heads(d, o, st, [(0, 9)])
+
+
 def test_long_context_slow_decay_split_matches_unsplit():
     """With long memory the entry states carried by the segment scan matter; a 64K-token
     sequence split into 8K segments must match the unsplit run and the oracle."""

@@ -171,6 +171,24 @@ def test_prefill_sequence_split_matches_oracle(dtype, chunk, seg):
     assert_close("S_T", st, s_ref, dtype)
 
 
+def test_prefill_automatic_split_with_longer_first_segment():
+    """The automatic plan splits a long sequence of few heads; segment 0 (run from S0 beside the
+    transition/increment pass of the middle segments) is longer than the others."""
+    kda = _kda()
+    T = 12288
+    seg, nvs = kda.prefill_plan(1, T, 1, 128, 128, 64)
+    assert nvs == 1 and seg < T and seg % 64 == 0
+    # workspace: transitions and increments of n - 1 segments plus n entry states
+    per_state = 128 * 128 * 4
+    n_seg = (kda.prefill_workspace_bytes(1, T, 1, 128, 128, 64) // per_state + 2) // 3
+    assert n_seg >= 3 and T - (n_seg - 1) * seg > seg   # the first segment holds the surplus
+    inp = _case(1, T, 1, 128, "bf16", decay="slow", s0=1.0, seed=31)
+    o, st = _run_prefill(inp, 64)
+    o_ref, s_ref = _oracle(inp)
+    assert_close("o", o, o_ref, "bf16")
+    assert_close("S_T", st, s_ref, "bf16")
+
+
 def test_prefill_column_split_matches_unsplit():
     inp = _case(1, 300, 3, 128, "bf16", seed=25)
     o1, s1 = _run_prefill(inp, 64, n_vs=1)
