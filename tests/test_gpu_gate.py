@@ -19,13 +19,14 @@ def _kda():
     return kda
 
 
-@pytest.mark.parametrize("T,chunk,seg,decay", [(700, 64, 0, "sig2"), (1000, 64, 256, "slow"),
-                                               (333, 32, 0, "sig2"), (200, 16, 0, "sig2")])
-def test_prefill_gate_matches_oracle(T, chunk, seg, decay):
+@pytest.mark.parametrize("B,T,chunk,seg,decay", [(2, 700, 64, 0, "sig2"), (2, 1000, 64, 256, "slow"),
+                                                 (2, 333, 32, 0, "sig2"), (2, 200, 16, 0, "sig2"),
+                                                 (1, 12288, 64, 0, "slow")])   # automatic split
+def test_prefill_gate_matches_oracle(B, T, chunk, seg, decay):
     kda = _kda()
-    print(f"gate T={T} chunk={chunk} seg={seg}", flush=True)
-    inp = gen.make_prefill_inputs(2, T, 2, 128, 128, "bf16", decay, 1.0, 110 + T, 0.0, "cpu")
-    g = gen.make_gate(2, T, 2, 128, "bf16", seed=110 + T)
+    print(f"gate B={B} T={T} chunk={chunk} seg={seg}", flush=True)
+    inp = gen.make_prefill_inputs(B, T, 2, 128, 128, "bf16", decay, 1.0, 110 + T, 0.0, "cpu")
+    g = gen.make_gate(B, T, 2, 128, "bf16", seed=110 + T)
     if decay == "slow":
         g = (g.float() - 8.0).to(torch.bfloat16)    # long memory: sigmoid(x) small
     dd = to_device(inp)

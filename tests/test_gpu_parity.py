@@ -161,9 +161,11 @@ def test_prefill_mixed_bound_tokens():
     assert_close("S_T", st, s_ref, "bf16")
 
 
-@pytest.mark.parametrize("dtype,chunk,seg", [("bf16", 64, 256), ("bf16", 32, 192), ("f32", 16, 128)])
+@pytest.mark.parametrize("dtype,chunk,seg", [("bf16", 64, 256), ("bf16", 32, 192), ("f32", 16, 128),
+                                             ("bf16", 64, 512), ("bf16", 64, 384), ("f32", 32, 512)])
 def test_prefill_sequence_split_matches_oracle(dtype, chunk, seg):
-    """Transitions + increments per segment, prefix scan, rerun from entry states."""
+    """Segment 0 from S0 beside the transitions + increments of the middle segments, prefix scan,
+    rerun from entry states.  T = 1000 gives 2 to 8 segments (2: no transition pass, no scan)."""
     inp = _case(2, 1000, 2, 128 if dtype == "bf16" else 64, dtype, decay="slow", s0=1.0, seed=24)
     o, st = _run_prefill(inp, chunk, seg_len=seg)
     o_ref, s_ref = _oracle(inp)
@@ -219,10 +221,11 @@ def test_prefill_in_place_state():
     assert_close("S_T", st, s_ref, "bf16")
 
 
-def test_prefill_in_place_state_with_split():
+@pytest.mark.parametrize("seg", [128, 320])
+def test_prefill_in_place_state_with_split(seg):
     inp = _case(1, 600, 2, 128, "bf16", decay="slow", s0=1.0, seed=27)
     o_ref, s_ref = _oracle(inp)
-    o, st = _run_prefill(inp, 64, seg_len=128, inplace=True)
+    o, st = _run_prefill(inp, 64, seg_len=seg, inplace=True)
     assert_close("o", o, o_ref, "bf16")
     assert_close("S_T", st, s_ref, "bf16")
 
