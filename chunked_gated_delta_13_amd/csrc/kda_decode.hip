@@ -15,7 +15,8 @@
 //   o  = S^T q = r + beta (k . q) e          no second pass over S
 // A workgroup owns one whole (sequence, head) state: DV/4 column groups of 4 (float4, so
 // each state row is read as one contiguous run) x 16 row groups.  Column sums are reduced
-// across the row groups of a wave with lane shuffles, then across the waves in LDS.  The
+// across the row groups of a wave with lane shuffles, then across the waves in LDS (one
+// barrier per token).  The
 // state a workgroup takes is chosen so that each of the 8 XCDs (which receive workgroups
 // round-robin) streams one contiguous range of states: a whole-state, XCD-contiguous
 // pattern moves measurably more bytes per second through HBM than half-state workgroups.
@@ -28,8 +29,10 @@
 
 namespace kda {
 
-// MM = most tokens per block this instantiation stages (1 for the decode step).
-template <int DK, typename TIn, int MM>
+// MM = most tokens per block this instantiation stages (1 for the decode step).  TWO = reduce
+// across the waves through workgroup totals with two barriers per token (blocks that write
+// outputs: the read-out sums then cost one LDS read per column) instead of one.
+template <int DK, typename TIn, int MM, bool TWO>
 __global__ __launch_bounds__(4 * DK) void kda_decode_kernel(const DecodeArgs a, int per_xcd) {
     constexpr int DV = DK;
     constexpr int NCG = DV / 4;      // float4 column groups per state row
@@ -80,9 +83,9 @@ __global__ __launch_bounds__(4 * DK) void kda_decode_kernel(const DecodeArgs a, 
         if (tid < mt) sbt[tid] = a.beta[tok_of(tid)];
     }
 
-    // per-wave column sums, then the workgroup totals (p, then r, then k.q)
-    __shared__ __attribute__((aligned(16))) float spart[NW][2 * DV + 4];
-    __shared__ float stot[2 * DV + 1];
+    // per-wave column sums (p, then r, then k.q), one buffer per token parity; workgroup totals
+    __shared__ __attribute__((aligned(16))) float spart[2][NW][2 * DV + 4];
+    __shared__ float stot[TWO ? 2 * DV + 1 : 1];
     if constexpr (MM > 1) __syncthreads();
 
     for (int t = 0; t < mt; ++t) {
@@ -124,28 +127,52 @@ __global__ __launch_bounds__(4 * DK) void kda_decode_kernel(const DecodeArgs a, 
             }
             kq += __shfl_xor(kq, off);
         }
-        // ... then over the waves: thread i <= 2 DV sums value i over the waves in order.  Two
-        // barriers per token keep the partials and totals single-buffered.
+        // ... then over the waves, in wave order.  With one barrier, every thread sums its own
+        // columns; the partials are double-buffered by token parity, so a wave writes token
+        // t+1's partials only after the barrier of token t, which every wave reaches after
+        // reading token t-1's.  With two, thread i <= 2 DV sums value i into the totals.
+        const int pb = TWO ? 0 : t & 1;
         if (lane < NCG) {
-            *reinterpret_cast<f32x4_t*>(&spart[wave][col]) = p;
-            *reinterpret_cast<f32x4_t*>(&spart[wave][DV + col]) = r;
+            *reinterpret_cast<f32x4_t*>(&spart[pb][wave][col]) = p;
+            *reinterpret_cast<f32x4_t*>(&spart[pb][wave][DV + col]) = r;
         }
-        if (lane == 0) spart[wave][2 * DV] = kq;
+        if (lane == 0) spart[pb][wave][2 * DV] = kq;
         __syncthreads();
-        if (tid <= 2 * DV) {
-            float acc = spart[0][tid];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) acc += spart[w][tid];
-            stot[tid] = acc;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = stot[col + j];
         const bool writes_o = a.o && rg == 0;
-        if (writes_o) {
+        if constexpr (TWO) {
+            if (tid <= 2 * DV) {
+                float acc = spart[0][0][tid];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) r[j] = stot[DV + col + j];
-            kq = stot[2 * DV];
+                for (int w = 1; w < NW; ++w) acc += spart[0][w][tid];
+                stot[tid] = acc;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[j] = stot[col + j];
+            if (writes_o) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) r[j] = stot[DV + col + j];
+                kq = stot[2 * DV];
+            }
+        } else {
+            p = *reinterpret_cast<const f32x4_t*>(&spart[pb][0][col]);
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&spart[pb][w][col]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p[j] += x[j];
+            }
+            if (writes_o) {
+                r = *reinterpret_cast<const f32x4_t*>(&spart[pb][0][DV + col]);
+                kq = spart[pb][0][2 * DV];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) {
+                    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&spart[pb][w][DV + col]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) r[j] += x[j];
+                    kq += spart[pb][w][2 * DV];
+                }
+            }
         }
 
         float bt;
@@ -180,14 +207,14 @@ __global__ __launch_bounds__(4 * DK) void kda_decode_kernel(const DecodeArgs a, 
     }
 }
 
-template <int MM>
+template <int MM, bool TWO>
 static hipError_t launch_decode_mm(int dk, bool f32, const DecodeArgs& a, dim3 grid, int per_xcd,
                                    hipStream_t stream) {
     const dim3 block(4 * dk);
-    if (dk == 128 && !f32) hipLaunchKernelGGL((kda_decode_kernel<128, __bf16, MM>), grid, block, 0, stream, a, per_xcd);
-    else if (dk == 128 && f32) hipLaunchKernelGGL((kda_decode_kernel<128, float, MM>), grid, block, 0, stream, a, per_xcd);
-    else if (dk == 64 && !f32) hipLaunchKernelGGL((kda_decode_kernel<64, __bf16, MM>), grid, block, 0, stream, a, per_xcd);
-    else if (dk == 64 && f32) hipLaunchKernelGGL((kda_decode_kernel<64, float, MM>), grid, block, 0, stream, a, per_xcd);
+    if (dk == 128 && !f32) hipLaunchKernelGGL((kda_decode_kernel<128, __bf16, MM, TWO>), grid, block, 0, stream, a, per_xcd);
+    else if (dk == 128 && f32) hipLaunchKernelGGL((kda_decode_kernel<128, float, MM, TWO>), grid, block, 0, stream, a, per_xcd);
+    else if (dk == 64 && !f32) hipLaunchKernelGGL((kda_decode_kernel<64, __bf16, MM, TWO>), grid, block, 0, stream, a, per_xcd);
+    else if (dk == 64 && f32) hipLaunchKernelGGL((kda_decode_kernel<64, float, MM, TWO>), grid, block, 0, stream, a, per_xcd);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -199,9 +226,13 @@ hipError_t launch_decode(int dk, bool f32, const DecodeArgs& a, hipStream_t stre
     const long long per_xcd = (a.NH + 7) / 8;
     if (per_xcd > 0x7fffffffLL / 8) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(8 * per_xcd));
-    if (a.m == 1) return launch_decode_mm<1>(dk, f32, a, grid, (int)per_xcd, stream);
-    if (a.m <= 4) return launch_decode_mm<4>(dk, f32, a, grid, (int)per_xcd, stream);
-    return launch_decode_mm<kDecodeMaxTokens>(dk, f32, a, grid, (int)per_xcd, stream);
+    // verify blocks (outputs, m > 1) reduce with two barriers per token, everything else with one
+    if (a.m == 1) return launch_decode_mm<1, false>(dk, f32, a, grid, (int)per_xcd, stream);
+    if (a.m <= 4)
+        return a.o ? launch_decode_mm<4, true>(dk, f32, a, grid, (int)per_xcd, stream)
+                   : launch_decode_mm<4, false>(dk, f32, a, grid, (int)per_xcd, stream);
+    return a.o ? launch_decode_mm<kDecodeMaxTokens, true>(dk, f32, a, grid, (int)per_xcd, stream)
+               : launch_decode_mm<kDecodeMaxTokens, false>(dk, f32, a, grid, (int)per_xcd, stream);
 }
 
 }  // namespace kda
