@@ -23,7 +23,9 @@
 // For an m-token block the state is read once, the m tokens run in order on
 // chip, and the state is written back only when the block is committed
 // ("Kimi K3's architecture", "The bill comes due in the serving stack": the
-// drafted tokens' inputs are kept and the state rebuilt from them).
+// drafted tokens' inputs are kept and the state rebuilt from them).  A verify
+// block of at most 4 tokens (outputs only) takes all its state reductions in
+// one pass instead (kda_verify_block_kernel).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -207,6 +209,182 @@ __global__ __launch_bounds__(4 * DK) void kda_decode_kernel(const DecodeArgs a, 
     }
 }
 
+// Speculative verify of a block of m <= MB tokens in one pass over the state (outputs only, the
+// state is not written).  With a_t = alpha_0 * ... * alpha_t (per key channel, t = 0 .. m-1) the
+// recurrence unrolls over the block to
+//   S_t = Diag(a_t) S + sum_{j <= t} beta_j Diag(a_t / a_j) k_j e_j^T,
+//   e_t = v_t - S^T (a_t . k_t) - sum_{j < t} G_tj e_j,     G_tj = beta_j sum_i (a_t/a_j)_i k_j,i k_t,i
+//   o_t = S^T (a_t . q_t) + sum_{j <= t} H_tj e_j,           H_tj = beta_j sum_i (a_t/a_j)_i k_j,i q_t,i
+// so the state is read once for 2m column sums, the m x m products G and H (independent of the
+// state) are formed while its loads are in flight, and e_t, o_t follow by forward substitution
+// per column.  a_t / a_j is formed as the product alpha_{j+1} ... alpha_t (no division); every
+// factor lies in [e^{-5 m}, 1].
+template <int DK, typename TIn, int MB>
+__global__ __launch_bounds__(4 * DK) void kda_verify_block_kernel(const DecodeArgs a, int per_xcd) {
+    constexpr int DV = DK;
+    constexpr int NCG = DV / 4, NRG = 16, NTH = NCG * NRG, NW = NTH / 64, RPT = DK / NRG;
+    constexpr int NP = MB * (MB + 1) / 2;   // (t, j) pairs with j <= t
+    constexpr int CPL = DK / 64;            // key channels per lane in the pair products
+    static_assert(NCG <= 64 && 64 % NCG == 0 && DK % 64 == 0, "a wave holds whole row groups");
+    const long long nh = (long long)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (nh >= a.NH) return;
+    const long long n = nh / a.H;
+    const int h = (int)(nh % a.H);
+    const int mt = a.m < MB ? a.m : MB;
+    const int tid = threadIdx.x;
+    const int cg = tid % NCG, rg = tid / NCG;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = cg * 4;
+
+    const float* Sb = a.S + nh * (long long)(DK * DV) + col;
+    f32x4_t s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(Sb + (long long)(rg + NRG * m) * DV));
+
+    __shared__ float skk[MB][DK], sqq[MB][DK], sal[MB][DK], sv[MB][DV], sbt[MB];
+    __shared__ float skt[MB][DK], sqt[MB][DK];   // a_t . k_t, a_t . q_t
+    __shared__ float sG[MB][MB], sH[MB][MB];
+    __shared__ __attribute__((aligned(16))) float spart[NW][2 * MB][DV];
+    __shared__ __attribute__((aligned(16))) float stot[2 * MB][DV];
+    auto tok_of = [&](int t) { return (n * a.m + t) * a.H + h; };   // token row of [N, m, H, *]
+    for (int e = tid; e < mt * DK; e += NTH) {
+        const int t = e / DK, i = e % DK;
+        const long long base = tok_of(t) * DK + i;
+        skk[t][i] = to_f32<TIn>(reinterpret_cast<const TIn*>(a.k)[base]);
+        sqq[t][i] = to_f32<TIn>(reinterpret_cast<const TIn*>(a.q)[base]);
+        sal[t][i] = __expf(fminf(fmaxf(a.log_alpha[base], kLogAlphaMin), 0.0f));
+    }
+    for (int e = tid; e < mt * DV; e += NTH) {
+        const int t = e / DV, c = e % DV;
+        sv[t][c] = to_f32<TIn>(reinterpret_cast<const TIn*>(a.v)[tok_of(t) * DV + c]);
+    }
+    if (tid < mt) sbt[tid] = a.beta[tok_of(tid)];
+    __syncthreads();
+
+    // decay-weighted keys and queries, and the pair products (wave w takes pairs w, w + NW, ...)
+    if (tid < DK) {
+        float at = 1.0f;
+        for (int t = 0; t < mt; ++t) {
+            at *= sal[t][tid];
+            skt[t][tid] = at * skk[t][tid];
+            sqt[t][tid] = at * sqq[t][tid];
+        }
+    }
+    for (int pp = wave; pp < NP; pp += NW) {
+        int t = 0;
+        while ((t + 1) * (t + 2) / 2 <= pp) ++t;
+        const int j = pp - t * (t + 1) / 2;   // j <= t
+        if (t >= mt) continue;                 // wave-uniform
+        float gs = 0.0f, hs = 0.0f;
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+            const int i = lane + 64 * u;
+            float c = sbt[j] * skk[j][i];
+            for (int l = j + 1; l <= t; ++l) c *= sal[l][i];
+            gs += c * skk[t][i];
+            hs += c * sqq[t][i];
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            gs += __shfl_xor(gs, off);
+            hs += __shfl_xor(hs, off);
+        }
+        if (lane == 0) {
+            sH[t][j] = hs;
+            if (j < t) sG[t][j] = gs;
+        }
+    }
+
+    // column sums of the state against the decay-weighted keys and queries
+    f32x4_t pk[MB], pq[MB];
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+        pk[t] = zero4();
+        pq[t] = zero4();
+    }
+    __syncthreads();   // skt, sqt (and sG, sH) complete
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+        if (t < mt) {
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const float kv = skt[t][rg + NRG * m], qv = sqt[t][rg + NRG * m];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    pk[t][jj] += s[m][jj] * kv;
+                    pq[t][jj] += s[m][jj] * qv;
+                }
+            }
+#pragma unroll
+            for (int off = NCG; off < 64; off <<= 1) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    pk[t][jj] += __shfl_xor(pk[t][jj], off);
+                    pq[t][jj] += __shfl_xor(pq[t][jj], off);
+                }
+            }
+            if (lane < NCG) {
+                *reinterpret_cast<f32x4_t*>(&spart[wave][2 * t][col]) = pk[t];
+                *reinterpret_cast<f32x4_t*>(&spart[wave][2 * t + 1][col]) = pq[t];
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < 2 * mt * DV; e += NTH) {
+        const int r = e / DV, c = e % DV;
+        float acc = spart[0][r][c];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) acc += spart[w][r][c];
+        stot[r][c] = acc;
+    }
+    __syncthreads();
+
+    // forward substitution per column: e_t, then o_t
+    if (rg == 0) {
+        f32x4_t ev[MB];
+#pragma unroll
+        for (int t = 0; t < MB; ++t) {
+            if (t < mt) {
+                const f32x4_t pt = *reinterpret_cast<const f32x4_t*>(&stot[2 * t][col]);
+                const f32x4_t qt = *reinterpret_cast<const f32x4_t*>(&stot[2 * t + 1][col]);
+                f32x4_t e4, o4;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) e4[jj] = sv[t][col + jj] - pt[jj];
+#pragma unroll
+                for (int j = 0; j < t; ++j) {
+                    const float g = sG[t][j];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) e4[jj] -= g * ev[j][jj];
+                }
+                ev[t] = e4;
+                o4 = qt;
+#pragma unroll
+                for (int j = 0; j <= t; ++j) {
+                    const float hh = sH[t][j];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) o4[jj] += hh * ev[j][jj];
+                }
+                TIn* on = reinterpret_cast<TIn*>(a.o) + tok_of(t) * DV + col;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) on[jj] = from_f32<TIn>(o4[jj]);
+            }
+        }
+    }
+}
+
+template <int MB>
+static hipError_t launch_verify_block(int dk, bool f32, const DecodeArgs& a, dim3 grid, int per_xcd,
+                                      hipStream_t stream) {
+    const dim3 block(4 * dk);
+    if (dk == 128 && !f32) hipLaunchKernelGGL((kda_verify_block_kernel<128, __bf16, MB>), grid, block, 0, stream, a, per_xcd);
+    else if (dk == 128 && f32) hipLaunchKernelGGL((kda_verify_block_kernel<128, float, MB>), grid, block, 0, stream, a, per_xcd);
+    else if (dk == 64 && !f32) hipLaunchKernelGGL((kda_verify_block_kernel<64, __bf16, MB>), grid, block, 0, stream, a, per_xcd);
+    else if (dk == 64 && f32) hipLaunchKernelGGL((kda_verify_block_kernel<64, float, MB>), grid, block, 0, stream, a, per_xcd);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 template <int MM, bool TWO>
 static hipError_t launch_decode_mm(int dk, bool f32, const DecodeArgs& a, dim3 grid, int per_xcd,
                                    hipStream_t stream) {
@@ -228,9 +406,12 @@ hipError_t launch_decode(int dk, bool f32, const DecodeArgs& a, hipStream_t stre
     const dim3 grid((unsigned)(8 * per_xcd));
     // verify blocks (outputs, m > 1) reduce with two barriers per token, everything else with one
     if (a.m == 1) return launch_decode_mm<1, false>(dk, f32, a, grid, (int)per_xcd, stream);
-    if (a.m <= 4)
+    if (a.m <= 4) {
+        // a verify block (outputs, state untouched, every sequence runs all m tokens) in one pass
+        if (a.o && !a.write_state && !a.lens) return launch_verify_block<4>(dk, f32, a, grid, (int)per_xcd, stream);
         return a.o ? launch_decode_mm<4, true>(dk, f32, a, grid, (int)per_xcd, stream)
                    : launch_decode_mm<4, false>(dk, f32, a, grid, (int)per_xcd, stream);
+    }
     return a.o ? launch_decode_mm<kDecodeMaxTokens, true>(dk, f32, a, grid, (int)per_xcd, stream)
                : launch_decode_mm<kDecodeMaxTokens, false>(dk, f32, a, grid, (int)per_xcd, stream);
 }

@@ -29,8 +29,9 @@ def _case(N, m, H, d, dtype, seed, s0=1.0, decay="sig2"):
     return inp
 
 
-@pytest.mark.parametrize("dtype,d,m", [("bf16", 128, 1), ("bf16", 128, 4), ("bf16", 128, 16),
-                                       ("bf16", 128, 24), ("bf16", 64, 40), ("f32", 64, 3),
+@pytest.mark.parametrize("dtype,d,m", [("bf16", 128, 1), ("bf16", 128, 2), ("bf16", 128, 4),
+                                       ("bf16", 64, 4), ("bf16", 128, 16), ("bf16", 128, 24),
+                                       ("bf16", 64, 40), ("f32", 64, 3), ("f32", 128, 4),
                                        ("f32", 128, 20)])
 def test_spec_verify_matches_oracle_and_keeps_state(dtype, d, m):
     kda = _kda()
