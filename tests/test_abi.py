@@ -183,11 +183,15 @@ def test_plan_rules(lib):
     assert lib.kda_chunk_prefill_plan(1, 1 << 20, 16, 128, 128, 32, F32, ctypes.byref(seg),
                                       ctypes.byref(nvs)) == OK
     assert nvs.value == 2 and seg.value % 32 == 0 and seg.value < (1 << 20)
-    # short sequence: never split below the minimum segment length
+    # short sequence: no split below three minimum segments (max(512, 8 sqrt(T)) tokens each)
+    assert lib.kda_chunk_prefill_plan(1, 1500, 1, 128, 128, 64, BF16, ctypes.byref(seg),
+                                      ctypes.byref(nvs)) == OK
+    assert seg.value == 1500
+    assert lib.kda_chunk_prefill_workspace_bytes(1, 1500, 1, 128, 128, 64, BF16, 0) == 0
+    # a few thousand tokens on one head: segments of at least the minimum length
     assert lib.kda_chunk_prefill_plan(1, 6000, 1, 128, 128, 64, BF16, ctypes.byref(seg),
                                       ctypes.byref(nvs)) == OK
-    assert seg.value == 6000
-    assert lib.kda_chunk_prefill_workspace_bytes(1, 6000, 1, 128, 128, 64, BF16, 0) == 0
+    assert 8 * 6000 ** 0.5 - 64 <= seg.value < 6000 / 3 and seg.value % 64 == 0
 
 
 def test_binding_refuses_host_tensors():
