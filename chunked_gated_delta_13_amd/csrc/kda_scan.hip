@@ -10,8 +10,10 @@
 // Entry state of segment s:  S_in(0) = S0,  S_in(s+1) = M_s S_in(s) + H_s.  With s_first = 1 the
 // walk starts from S_in(1), already written by the pass that ran segment 0 from S0.
 // State columns are independent, so a workgroup owns (head, 16 columns) and
-// keeps that column block of S_in in LDS while it walks the segments.  fp32
-// throughout; the n_seg - 1 steps are tiny next to the chunk passes around them.
+// keeps that column block of S_in in LDS while it walks the segments; each
+// thread holds one row of the step's transition in registers (the next step's
+// row is requested before the current step's products).  fp32 throughout, with
+// each entry summed over m in order (the same sums as one row-by-row product).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -22,51 +24,91 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(const ScanArgs a) {
     constexpr int CB = 16;               // columns per workgroup
     constexpr int NCB = DK / CB;
     constexpr int TPR = 256 / DK;        // threads per row
-    constexpr int CPT = CB / TPR;        // columns per thread
+    constexpr int CPT = CB / TPR;        // columns per thread (8 or 4)
+    constexpr int NQ = CPT / 4;          // float4 groups per thread
+    static_assert(CPT % 4 == 0, "whole float4 column groups per thread");
     const int bh = blockIdx.x / NCB;
     const int cb = blockIdx.x % NCB;
     if (bh >= a.BH) return;
     const int tid = threadIdx.x;
     const int row = tid / TPR;
-    const int c0 = cb * CB + (tid % TPR) * CPT;
+    const int cl = (tid % TPR) * CPT;    // first column of this thread inside the block
+    const int c0 = cb * CB + cl;
     constexpr long long SS = (long long)DK * DK;
 
-    __shared__ float sS[DK][CB + 1];
-    float cur[CPT];
+    // the current entry state's column block, rows 16-byte aligned (every lane of a wave reads the
+    // same row at a time: broadcast reads)
+    __shared__ __attribute__((aligned(16))) float sS[DK][CB];
+    f32x4_t cur[NQ];
     float* sin = a.S_in + (long long)bh * a.n_seg * SS;
     if (a.s_first == 0) {
         const float* s0 = a.S0 ? a.S0 + bh * SS : nullptr;
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) cur[j] = s0 ? s0[(long long)row * DK + c0 + j] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) sin[(long long)row * DK + c0 + j] = cur[j];
+        for (int q = 0; q < NQ; ++q) {
+            cur[q] = s0 ? *reinterpret_cast<const f32x4_t*>(s0 + (long long)row * DK + c0 + 4 * q) : zero4();
+            *reinterpret_cast<f32x4_t*>(sin + (long long)row * DK + c0 + 4 * q) = cur[q];
+        }
     } else {
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) cur[j] = sin[(long long)a.s_first * SS + (long long)row * DK + c0 + j];
+        for (int q = 0; q < NQ; ++q)
+            cur[q] = *reinterpret_cast<const f32x4_t*>(sin + (long long)a.s_first * SS + (long long)row * DK + c0 + 4 * q);
     }
 
+    // row `row` of M_s and this thread's columns of H_s, for the step being computed and the next
+    auto mrow_of = [&](int s) { return a.M + ((long long)bh * (a.n_seg - 1) + s) * SS + (long long)row * DK; };
+    auto hrow_of = [&](int s) { return a.Hinc + ((long long)bh * (a.n_seg - 1) + s) * SS + (long long)row * DK + c0; };
+    f32x4_t mr[DK / 4], hr[NQ];
+    if (a.s_first + 1 < a.n_seg) {
+        const float* M = mrow_of(a.s_first);
+        const float* Hs = hrow_of(a.s_first);
+#pragma unroll
+        for (int m = 0; m < DK / 4; ++m) mr[m] = *reinterpret_cast<const f32x4_t*>(M + 4 * m);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) hr[q] = *reinterpret_cast<const f32x4_t*>(Hs + 4 * q);
+    }
     for (int s = a.s_first; s + 1 < a.n_seg; ++s) {
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) sS[row][c0 - cb * CB + j] = cur[j];
+        for (int q = 0; q < NQ; ++q) *reinterpret_cast<f32x4_t*>(&sS[row][cl + 4 * q]) = cur[q];
         __syncthreads();
-        const float* M = a.M + ((long long)bh * (a.n_seg - 1) + s) * SS + (long long)row * DK;
-        const float* Hs = a.Hinc + ((long long)bh * (a.n_seg - 1) + s) * SS + (long long)row * DK;
-        float acc[CPT];
+        // next step's operands requested before this step's products
+        f32x4_t mn[DK / 4], hn[NQ];
+        const bool more = s + 2 < a.n_seg;
+        if (more) {
+            const float* M = mrow_of(s + 1);
+            const float* Hs = hrow_of(s + 1);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) acc[j] = Hs[c0 + j];
-        for (int m = 0; m < DK; m += 4) {
-            const f32x4_t mv = *reinterpret_cast<const f32x4_t*>(M + m);
+            for (int m = 0; m < DK / 4; ++m) mn[m] = *reinterpret_cast<const f32x4_t*>(M + 4 * m);
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int q = 0; q < NQ; ++q) hn[q] = *reinterpret_cast<const f32x4_t*>(Hs + 4 * q);
+        }
+        f32x4_t acc[NQ];
 #pragma unroll
-                for (int j = 0; j < CPT; ++j) acc[j] += mv[u] * sS[m + u][c0 - cb * CB + j];
+        for (int q = 0; q < NQ; ++q) acc[q] = hr[q];
+#pragma unroll
+        for (int m = 0; m < DK / 4; ++m) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float mv = mr[m][u];
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(&sS[4 * m + u][cl + 4 * q]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[q][j] += mv * sv[j];
+                }
+            }
         }
         float* dst = sin + (long long)(s + 1) * SS + (long long)row * DK + c0;
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            cur[j] = acc[j];
-            dst[j] = acc[j];
+        for (int q = 0; q < NQ; ++q) {
+            cur[q] = acc[q];
+            *reinterpret_cast<f32x4_t*>(dst + 4 * q) = acc[q];
+        }
+        if (more) {
+#pragma unroll
+            for (int m = 0; m < DK / 4; ++m) mr[m] = mn[m];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) hr[q] = hn[q];
         }
     }
 }
