@@ -29,7 +29,10 @@
  *  - Layouts are contiguous row-major.  Pointers must be 16-byte aligned
  *    (beta: 4-byte aligned).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
- *    asynchronously; no call synchronises the host with the device.
+ *    asynchronously; no call synchronises the host with the device.  A split
+ *    prefill also uses one stream of the library's own per device (created on
+ *    first use, default priority, kept for the life of the process), forked
+ *    from and joined back to `stream` by events.
  *  - Arguments are validated on the host before anything is enqueued; a
  *    rejected call returns an error status and enqueues nothing.  A launch
  *    failure returns KDA_ERR_DEVICE.  Valid inputs produce no in-kernel errors.
