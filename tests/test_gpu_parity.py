@@ -192,6 +192,46 @@ def test_prefill_automatic_split(T, H):
     assert_close("S_T", st, s_ref, "bf16")
 
 
+def test_prefill_split_from_two_host_threads():
+    """Split prefills enqueued from two host threads at once, each on its own stream, share the
+    library's side stream and fork/join events; each result equals the same call made alone."""
+    import threading
+    kda = _kda()
+    cases = [to_device(_case(1, 4096, 2, 128, "bf16", decay="slow", s0=1.0, seed=s)) for s in (61, 62)]
+    assert kda.prefill_plan(1, 4096, 2, 128, 128, 64)[0] < 4096   # the automatic plan splits
+    refs = []
+    for d in cases:
+        o, st = kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"], chunk=64)
+        refs.append((o, st))
+    torch.cuda.synchronize()
+    outs = [[], []]
+    errors = []
+
+    def run(i):
+        try:
+            stream = torch.cuda.Stream()
+            d = cases[i]
+            with torch.cuda.stream(stream):
+                for _ in range(6):
+                    outs[i].append(kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                                                     d["S0"], chunk=64))
+            stream.synchronize()
+        except Exception as e:   # reported below, in the test's own thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in (0, 1)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in (0, 1):
+        assert len(outs[i]) == 6
+        for o, st in outs[i]:
+            assert torch.equal(o, refs[i][0]) and torch.equal(st, refs[i][1])
+
+
 def test_prefill_column_split_matches_unsplit():
     inp = _case(1, 300, 3, 128, "bf16", seed=25)
     o1, s1 = _run_prefill(inp, 64, n_vs=1)
