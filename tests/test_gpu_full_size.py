@@ -85,17 +85,31 @@ def test_long_context_automatic_plan_sampled_head():
 
 
 def test_long_context_slow_decay_split_matches_unsplit():
-    """With long memory the entry states carried by the segment scan matter; a 64K-token
-    sequence split into 8K segments must match the unsplit run and the oracle."""
+    """A 64K-token sequence with very slow decay (the slow recipe scaled by 0.01) split into 8K
+    segments matches the unsplit run and the oracle.  The delta write itself forgets (each token
+    shrinks the state along its key), so over an 8K segment the entry state reaches the segment's
+    end only as rounding noise; it shapes the outputs right after each boundary instead.  Those
+    must follow the entry state the scan delivered: run from a zero state they would differ."""
     kda = _kda()
-    d = gen.make_prefill_inputs(1, 65536, 2, 128, 128, "bf16", "slow", 1.0, seed=41,
-                                bound_frac=0.1, device="cuda")
+    T, seg, w = 65536, 8192, 256
+    d = gen.make_prefill_inputs(1, T, 2, 128, 128, "bf16", "slow", 1.0, seed=41,
+                                bound_frac=0.0, device="cuda")
+    d["log_alpha"].mul_(0.01)
     o1, s1 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
-                               chunk=64, seg_len=8192)
+                               chunk=64, seg_len=seg)
     o2, s2 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
-                               chunk=64)
+                               chunk=64, seg_len=1 << 30)   # one pass, no split
+    cut = lambda x: x[:, seg:seg + w].contiguous()   # noqa: E731  (the first tokens of segment 1)
+    oz, _ = kda.chunk_prefill(cut(d["q"]), cut(d["k"]), cut(d["v"]), cut(d["log_alpha"]),
+                              cut(d["beta"]), None, chunk=64)
     torch.cuda.synchronize()
     assert_close("S_T split vs unsplit", s1, to_f64(s2), "bf16")
+    assert_close("o split vs unsplit", o1, to_f64(o2), "bf16")
+    assert_close("o after the first boundary, split vs unsplit", cut(o1), to_f64(cut(o2)), "bf16")
+    ref = cut(o2).double()
+    gap = float(torch.linalg.vector_norm(oz.double() - ref) / torch.linalg.vector_norm(ref))
+    print(f"  outputs after the boundary from a zero entry state: rel-L2 {gap:.3e}", flush=True)
+    assert gap > 0.05
     _check_heads(d, o1, s1, [(0, 1)])
 
 
