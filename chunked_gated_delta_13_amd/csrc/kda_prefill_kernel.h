@@ -538,14 +538,13 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                     const float x = fast_exp2(loc);              // <= 1
                     const float y = fast_exp2(-loc);             // >= 1, at most 2^115.4 = e^80
                     const float kv = QI::get(pk[i], u);
-                    const float xe = x * er[u];                  // 2^{g} <= 1
                     if constexpr (!DUAL) {
                         const float qv = QI::get(pq[i], u);
                         lq[u] = qv * x;
-                        qt[u] = qv * xe;
+                        qt[u] = lq[u] * er[u];                  // q 2^{g}: 2^{g - rho_a} 2^{rho_a}
                     }
                     lk[u] = kv * x;
-                    kt[u] = kv * xe;
+                    kt[u] = lk[u] * er[u];
                     kd[u] = kv * y;
                     // K' = k 2^{g_C - g}: the factor above 1 meets only a factor that cannot underflow
                     kp[u][i] = (kd[u] * fd[u]) * fc[u];

@@ -412,11 +412,10 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
                     const float y = fast_exp2(-loc);
                     const float kv = QI::get(pk[i], e);
                     const float qv = QI::get(pq[i], e);
-                    const float xe = x * er[e];
                     lq[e] = qv * x;
-                    qt[e] = qv * xe;
+                    qt[e] = lq[e] * er[e];   // q 2^{g} = (q 2^{g - rho_a}) 2^{rho_a}
                     lk[e] = kv * x;
-                    kt[e] = kv * xe;
+                    kt[e] = lk[e] * er[e];
                     kd[e] = kv * y;
                     const float kpv = (kd[e] * fd[e]) * fc[e];
                     if (i & 1) kp[e][i / 2] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)kpv) << 16;
