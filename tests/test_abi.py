@@ -194,6 +194,44 @@ def test_plan_rules(lib):
     assert 8 * 6000 ** 0.5 - 64 <= seg.value < 6000 / 3 and seg.value % 64 == 0
 
 
+def test_automatic_plan_properties(lib):
+    """Over a sweep of shapes the automatic plan keeps its rules: segments are whole chunks that
+    cover the sequence; a split has at least 3 segments, each phase of it fits in fewer workgroups
+    than the 256 compute units (units * (n - 1) <= 255), its segments are not much shorter than
+    max(512, 8 sqrt(T)) and the first takes what the others leave (at most about twice their
+    length); shapes that already fill the chip, or are too short, are not split.  The
+    workspace matches the plan (transition + increment per segment but the last, entry states)."""
+    import itertools
+    import math
+    seg = ctypes.c_int(0)
+    nvs = ctypes.c_int(0)
+    lib.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
+    checked = 0
+    for B, H, T, d, (dt, chunk) in itertools.product(
+            (1, 2, 4), (1, 2, 8, 16, 56), (1, 100, 1000, 1536, 4096, 6000, 12288, 65536, 1 << 20),
+            (64, 128), ((BF16, 64), (BF16, 32), (F32, 16), (F32, 32))):
+        assert lib.kda_chunk_prefill_plan(B, T, H, d, d, chunk, dt, ctypes.byref(seg),
+                                          ctypes.byref(nvs)) == OK
+        L, vs = seg.value, nvs.value
+        units = B * H * vs
+        ws = lib.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, chunk, dt, 0)
+        lmin = max(512, 8 * math.sqrt(T))
+        if L >= T:   # no split
+            assert ws == 0
+            assert 2 * units > 255 or T < 3 * lmin or (255 // units) < 2, (B, H, T, d, dt, chunk)
+            continue
+        per = B * H * d * d * 4
+        assert ws % per == 0 and (ws // per + 2) % 3 == 0, (B, H, T, d, dt, chunk, ws)
+        n = (ws // per + 2) // 3
+        assert L % chunk == 0 and L >= 0.5 * lmin, (B, H, T, d, dt, chunk, L)
+        assert n >= 3 and units * (n - 1) <= 255, (B, H, T, d, dt, chunk, n)
+        # segment 0 takes what the others leave: more than nothing, at most about the cost ratio
+        # of the two passes (<= 2) times L, plus half a chunk of rounding per segment
+        assert 0 < T - (n - 1) * L <= 2 * L + n * chunk, (B, H, T, d, dt, chunk, n, L)
+        checked += 1
+    assert checked > 20   # the sweep does reach the split branch
+
+
 def test_binding_refuses_host_tensors():
     import torch
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
