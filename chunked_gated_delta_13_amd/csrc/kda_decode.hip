@@ -236,6 +236,21 @@ __global__ __launch_bounds__(4 * DK) void kda_verify_block_kernel(const DecodeAr
     const int lane = tid & 63, wave = tid >> 6;
     const int col = cg * 4;
 
+    // The block's token inputs (one element of each per thread) are requested before the state,
+    // so that staging them and the pair products, which need nothing else, run while the state
+    // is still arriving.  Threads past the block's last element read element 0 and discard it.
+    static_assert(MB * DK <= NTH, "one input element per thread");
+    auto tok_of = [&](int t) { return (n * a.m + t) * a.H + h; };   // token row of [N, m, H, *]
+    const bool has_in = tid < mt * DK;
+    const int te = has_in ? tid / DK : 0, ie = has_in ? tid % DK : 0;
+    const long long ibase = tok_of(te) * DK + ie;                   // DV == DK
+    const TIn kin = reinterpret_cast<const TIn*>(a.k)[ibase];
+    const TIn qin = reinterpret_cast<const TIn*>(a.q)[ibase];
+    const TIn vin = reinterpret_cast<const TIn*>(a.v)[ibase];
+    const float lin = a.log_alpha[ibase];
+    const float bin = a.beta[tok_of(tid < mt ? tid : 0)];
+    __builtin_amdgcn_sched_barrier(0);   // keep these requests ahead of the state's
+
     const float* Sb = a.S + nh * (long long)(DK * DV) + col;
     f32x4_t s[RPT];
 #pragma unroll
@@ -247,20 +262,14 @@ __global__ __launch_bounds__(4 * DK) void kda_verify_block_kernel(const DecodeAr
     __shared__ float sG[MB][MB], sH[MB][MB];
     __shared__ __attribute__((aligned(16))) float spart[NW][2 * MB][DV];
     __shared__ __attribute__((aligned(16))) float stot[2 * MB][DV];
-    auto tok_of = [&](int t) { return (n * a.m + t) * a.H + h; };   // token row of [N, m, H, *]
-    for (int e = tid; e < mt * DK; e += NTH) {
-        const int t = e / DK, i = e % DK;
-        const long long base = tok_of(t) * DK + i;
-        skk[t][i] = to_f32<TIn>(reinterpret_cast<const TIn*>(a.k)[base]);
-        sqq[t][i] = to_f32<TIn>(reinterpret_cast<const TIn*>(a.q)[base]);
-        sal[t][i] = __expf(fminf(fmaxf(a.log_alpha[base], kLogAlphaMin), 0.0f));
+    if (has_in) {
+        skk[te][ie] = to_f32<TIn>(kin);
+        sqq[te][ie] = to_f32<TIn>(qin);
+        sal[te][ie] = __expf(fminf(fmaxf(lin, kLogAlphaMin), 0.0f));
+        sv[te][ie] = to_f32<TIn>(vin);
     }
-    for (int e = tid; e < mt * DV; e += NTH) {
-        const int t = e / DV, c = e % DV;
-        sv[t][c] = to_f32<TIn>(reinterpret_cast<const TIn*>(a.v)[tok_of(t) * DV + c]);
-    }
-    if (tid < mt) sbt[tid] = a.beta[tok_of(tid)];
-    __syncthreads();
+    if (tid < mt) sbt[tid] = bin;
+    barrier_lds();   // the state loads stay in flight
 
     // decay-weighted keys and queries, and the pair products (wave w takes pairs w, w + NW, ...)
     if (tid < DK) {
@@ -303,7 +312,7 @@ __global__ __launch_bounds__(4 * DK) void kda_verify_block_kernel(const DecodeAr
         pk[t] = zero4();
         pq[t] = zero4();
     }
-    __syncthreads();   // skt, sqt (and sG, sH) complete
+    barrier_lds();   // skt, sqt (and sG, sH) complete; the state loads may still be in flight
 #pragma unroll
     for (int t = 0; t < MB; ++t) {
         if (t < mt) {
