@@ -220,7 +220,7 @@ __global__ __launch_bounds__(4 * DK) void kda_decode_kernel(const DecodeArgs a, 
 // per column.  a_t / a_j is formed as the product alpha_{j+1} ... alpha_t (no division); every
 // factor lies in [e^{-5 m}, 1].
 template <int DK, typename TIn, int MB>
-__global__ __launch_bounds__(4 * DK) void kda_verify_block_kernel(const DecodeArgs a, int per_xcd) {
+__global__ __launch_bounds__(4 * DK) __attribute__((amdgpu_waves_per_eu(8))) void kda_verify_block_kernel(const DecodeArgs a, int per_xcd) {
     constexpr int DV = DK;
     constexpr int NCG = DV / 4, NRG = 16, NTH = NCG * NRG, NW = NTH / 64, RPT = DK / NRG;
     constexpr int NP = MB * (MB + 1) / 2;   // (t, j) pairs with j <= t
@@ -260,7 +260,8 @@ __global__ __launch_bounds__(4 * DK) void kda_verify_block_kernel(const DecodeAr
     __shared__ float skk[MB][DK], sqq[MB][DK], sal[MB][DK], sv[MB][DV], sbt[MB];
     __shared__ float skt[MB][DK], sqt[MB][DK];   // a_t . k_t, a_t . q_t
     __shared__ float sG[MB][MB], sH[MB][MB];
-    __shared__ __attribute__((aligned(16))) float spart[NW][2 * MB][DV];
+    constexpr int HB = MB < 2 ? MB : 2;   // tokens per group of column sums
+    __shared__ __attribute__((aligned(16))) float spart[NW][2 * HB][DV];
     __shared__ __attribute__((aligned(16))) float stot[2 * MB][DV];
     if (has_in) {
         skk[te][ie] = to_f32<TIn>(kin);
@@ -305,49 +306,52 @@ __global__ __launch_bounds__(4 * DK) void kda_verify_block_kernel(const DecodeAr
         }
     }
 
-    // column sums of the state against the decay-weighted keys and queries
-    f32x4_t pk[MB], pq[MB];
-#pragma unroll
-    for (int t = 0; t < MB; ++t) {
-        pk[t] = zero4();
-        pq[t] = zero4();
-    }
+    // column sums of the state against the decay-weighted keys and queries, HB tokens at a time
+    // (the per-wave partials of a group are summed into the totals before the next group's are
+    // written, which keeps the partials buffer, and so the workgroup's LDS, small)
     barrier_lds();   // skt, sqt (and sG, sH) complete; the state loads may still be in flight
 #pragma unroll
-    for (int t = 0; t < MB; ++t) {
-        if (t < mt) {
+    for (int t0 = 0; t0 < MB; t0 += HB) {
+        if (t0 >= mt) break;   // uniform
 #pragma unroll
-            for (int m = 0; m < RPT; ++m) {
-                const float kv = skt[t][rg + NRG * m], qv = sqt[t][rg + NRG * m];
+        for (int u = 0; u < HB; ++u) {
+            const int t = t0 + u;
+            if (t < mt) {
+                f32x4_t pk = zero4(), pq = zero4();
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    pk[t][jj] += s[m][jj] * kv;
-                    pq[t][jj] += s[m][jj] * qv;
+                for (int m = 0; m < RPT; ++m) {
+                    const float kv = skt[t][rg + NRG * m], qv = sqt[t][rg + NRG * m];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        pk[jj] += s[m][jj] * kv;
+                        pq[jj] += s[m][jj] * qv;
+                    }
                 }
-            }
 #pragma unroll
-            for (int off = NCG; off < 64; off <<= 1) {
+                for (int off = NCG; off < 64; off <<= 1) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    pk[t][jj] += __shfl_xor(pk[t][jj], off);
-                    pq[t][jj] += __shfl_xor(pq[t][jj], off);
+                    for (int jj = 0; jj < 4; ++jj) {
+                        pk[jj] += __shfl_xor(pk[jj], off);
+                        pq[jj] += __shfl_xor(pq[jj], off);
+                    }
                 }
-            }
-            if (lane < NCG) {
-                *reinterpret_cast<f32x4_t*>(&spart[wave][2 * t][col]) = pk[t];
-                *reinterpret_cast<f32x4_t*>(&spart[wave][2 * t + 1][col]) = pq[t];
+                if (lane < NCG) {
+                    *reinterpret_cast<f32x4_t*>(&spart[wave][2 * u][col]) = pk;
+                    *reinterpret_cast<f32x4_t*>(&spart[wave][2 * u + 1][col]) = pq;
+                }
             }
         }
-    }
-    __syncthreads();
-    for (int e = tid; e < 2 * mt * DV; e += NTH) {
-        const int r = e / DV, c = e % DV;
-        float acc = spart[0][r][c];
+        barrier_lds();
+        const int nt = mt - t0 < HB ? mt - t0 : HB;
+        for (int e = tid; e < 2 * nt * DV; e += NTH) {
+            const int r = e / DV, c = e % DV;
+            float acc = spart[0][r][c];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) acc += spart[w][r][c];
-        stot[r][c] = acc;
+            for (int w = 1; w < NW; ++w) acc += spart[w][r][c];
+            stot[2 * t0 + r][c] = acc;
+        }
+        barrier_lds();
     }
-    __syncthreads();
 
     // forward substitution per column: e_t, then o_t
     if (rg == 0) {
