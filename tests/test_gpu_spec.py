@@ -46,8 +46,9 @@ def test_spec_verify_matches_oracle_and_keeps_state(dtype, d, m):
     assert_close("o", o, o_ref, dtype)
 
 
-@pytest.mark.parametrize("dtype,d,m", [("bf16", 128, 4), ("bf16", 128, 16), ("bf16", 64, 33),
-                                       ("f32", 64, 5), ("f32", 128, 17)])
+@pytest.mark.parametrize("dtype,d,m", [("bf16", 128, 4), ("bf16", 128, 2), ("bf16", 64, 3),
+                                       ("f32", 128, 4), ("f32", 64, 2), ("bf16", 128, 16),
+                                       ("bf16", 64, 33), ("f32", 64, 5), ("f32", 128, 17)])
 def test_spec_commit_matches_oracle(dtype, d, m):
     kda = _kda()
     print(f"spec commit dtype={dtype} d={d} m={m}", flush=True)
