@@ -58,6 +58,26 @@ __global__ __launch_bounds__(4 * DK) void kda_decode_kernel(const DecodeArgs a, 
     const int lane = tid & 63, wave = tid >> 6;
     const int col = cg * 4;
 
+    auto tok_of = [&](int t) { return (n * a.m + t) * a.H + h; };   // token row of [N, m, H, *]
+    auto alpha_of = [](float la) { return __expf(fminf(fmaxf(la, kLogAlphaMin), 0.0f)); };
+    // Blocks of at most NTH / DK tokens hold one element of each input per thread: those are
+    // requested ahead of the state, so that staging them overlaps the state's arrival.  Threads
+    // past the block's last element read element 0 and discard it.
+    constexpr bool EARLY = MM > 1 && MM * DK <= NTH;
+    const bool has_in = EARLY && tid < mt * DK;
+    const int te = has_in ? tid / DK : 0, ie = has_in ? tid % DK : 0;
+    TIn kin{}, qin{}, vin{};
+    float lin = 0.0f, bin = 0.0f;
+    if constexpr (EARLY) {
+        const long long ibase = tok_of(te) * DK + ie;   // DV == DK
+        kin = reinterpret_cast<const TIn*>(a.k)[ibase];
+        qin = reinterpret_cast<const TIn*>(a.q)[ibase];
+        vin = reinterpret_cast<const TIn*>(a.v)[ibase];
+        lin = a.log_alpha[ibase];
+        bin = a.beta[tok_of(tid < mt ? tid : 0)];
+        __builtin_amdgcn_sched_barrier(0);   // keep these requests ahead of the state's
+    }
+
     float* Sb = a.S + nh * (long long)(DK * DV) + col;
     f32x4_t s[RPT];
 #pragma unroll
@@ -68,9 +88,15 @@ __global__ __launch_bounds__(4 * DK) void kda_decode_kernel(const DecodeArgs a, 
     // single token (the decode step) is read straight from memory.
     constexpr int MS = MM > 1 ? MM : 1;
     __shared__ float skk[MS][DK], sqq[MS][DK], sal[MS][DK], sv[MS][DV], sbt[MS];
-    auto tok_of = [&](int t) { return (n * a.m + t) * a.H + h; };   // token row of [N, m, H, *]
-    auto alpha_of = [](float la) { return __expf(fminf(fmaxf(la, kLogAlphaMin), 0.0f)); };
-    if constexpr (MM > 1) {
+    if constexpr (EARLY) {
+        if (has_in) {
+            skk[te][ie] = to_f32<TIn>(kin);
+            sqq[te][ie] = to_f32<TIn>(qin);
+            sal[te][ie] = alpha_of(lin);
+            sv[te][ie] = to_f32<TIn>(vin);
+        }
+        if (tid < mt) sbt[tid] = bin;
+    } else if constexpr (MM > 1) {
         for (int e = tid; e < mt * DK; e += NTH) {
             const int t = e / DK, i = e % DK;
             const long long base = tok_of(t) * DK + i;
