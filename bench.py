@@ -35,6 +35,8 @@ BYTES_PER_TOKEN_HEAD = 1540
 # Useful multiply-adds per token-head: five lower-triangular 16-token-tile products
 # (5 * (n+1)/2 * 16 * d with n = 4) + three state products (3 d^2) + the inverse (~1067).
 FLOPS_PER_TOKEN_HEAD = 2 * (5 * 2.5 * 16 * 128 + 3 * 128 * 128 + 1067)
+# the kernel that runs the model-width workload (one 128-column slice per workgroup)
+PREFILL_KERNEL = "kda_prefill_pipe_kernel<8,false>"
 # sources of the model-width prefill kernel (a profile's counters hold while their hash matches)
 PREFILL_SOURCES = ["kda_prefill_pipe.h", "kda_prefill_kernel.h", "kda_device.h"]
 
@@ -115,7 +117,7 @@ def bench_prefill(kda, gen, steps, warmup):
     assert torch.isfinite(o[:, -64:].float()).all() and torch.isfinite(st).all()
     plan = kda.prefill_plan(w.B, w.T, w.H, w.dk, w.dv, w.chunk)
     log(f"[prefill] {steps} steps: wall {wall*1e3:.2f} ms, events {ev*1e3:.2f} ms, plan {plan}")
-    return w, d, wall, ev, plan
+    return w, d, wall, ev, plan, o
 
 
 def bench_prefill_ckpt(kda, w, d, steps, warmup, every=4096):
@@ -191,25 +193,32 @@ def bench_long(kda, gen, steps, warmup):
     return w, res
 
 
-def bench_decode(kda, gen, steps=1000, pool=8):
+def bench_decode(kda, gen, steps=1000, warmup=10):
+    """The decode workload as defined: `steps` consecutive steps, step s with its own seeded
+    token inputs (seed 4 * 10^6 + s), all drawn on the device before the timed region; the
+    warm-up steps use further seeds."""
     import torch
     w = gen.DECODE_WORKLOADS["decode_n256"]
-    log(f"[decode] {w.note}: state {w.N*w.H*w.dk*w.dv*4/1e9:.3f} GB, {pool} distinct token sets")
+    log(f"[decode] {w.note}: state {w.N*w.H*w.dk*w.dv*4/1e9:.3f} GB, {steps} + {warmup} distinct token sets")
     S = gen.make_state(w.N, w.H, w.dk, w.dv, w.s0_std, seed=w.seed, device="cuda")
-    toks = [gen.make_decode_inputs(w.N, w.H, w.dk, w.dv, w.dtype, w.decay, seed=w.seed * 10**6 + i,
-                                   device="cuda") for i in range(pool)]
+    seeds = [w.seed * 10**6 + steps + i for i in range(warmup)] + [w.seed * 10**6 + i for i in range(steps)]
+    toks = [gen.make_decode_inputs(w.N, w.H, w.dk, w.dv, w.dtype, w.decay, seed=sd, device="cuda")
+            for sd in seeds]
     o = torch.empty((w.N, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
     it = [0]
 
     def step():
-        t = toks[it[0] % pool]
+        t = toks[it[0]]
         it[0] += 1
         kda.decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], S, o=o)
 
-    wall, ev = time_loop(step, steps, 10, stream)
+    wall, ev = time_loop(step, steps, warmup, stream)
+    assert it[0] == steps + warmup
     assert torch.isfinite(S).all()
     log(f"[decode] {steps} steps: wall {wall*1e3:.2f} ms, events {ev*1e3:.2f} ms")
+    del toks, S
+    torch.cuda.empty_cache()
     return w, wall, ev
 
 
@@ -225,9 +234,12 @@ def spec_bytes(N, H, d, m, accepted):
     return verify, commit
 
 
-def bench_spec(kda, gen, steps=200, pool=8):
+def bench_spec(kda, gen, steps=200, warmup=5):
+    """The speculative-decoding workload: every timed step on its own seeded drafted block (block
+    i with seed 7 * 10^6 + i), all drawn on the device before the timed regions."""
     import torch
     w = gen.SPEC_WORKLOADS["spec_n256_m4"]
+    pool = steps + warmup
     log(f"[spec] {w.note}: state {w.N*w.H*w.dk*w.dv*4/1e9:.3f} GB, {pool} distinct drafted blocks")
     S = gen.make_state(w.N, w.H, w.dk, w.dv, w.s0_std, seed=w.seed, device="cuda")
     blocks = [gen.make_spec_inputs(w.N, w.m, w.H, w.dk, w.dv, w.dtype, w.decay,
@@ -252,9 +264,11 @@ def bench_spec(kda, gen, steps=200, pool=8):
         kda.spec_verify(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], S, o=o)
         kda.spec_commit(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], S, b["accepted"])
 
-    _, ev_v = time_loop(verify, steps, 5, stream)
-    _, ev_c = time_loop(commit, steps, 5, stream)
-    wall, ev_b = time_loop(both, steps, 5, stream)
+    _, ev_v = time_loop(verify, steps, warmup, stream)
+    it[0] = 0
+    _, ev_c = time_loop(commit, steps, warmup, stream)
+    it[0] = 0
+    wall, ev_b = time_loop(both, steps, warmup, stream)
     assert torch.isfinite(S).all()
     acc_mean = sum(float(b["accepted"].float().mean()) for b in blocks) / pool
     per = [spec_bytes(w.N, w.H, w.dk, w.m, b["accepted"].cpu()) for b in blocks]
@@ -269,12 +283,26 @@ def bench_spec(kda, gen, steps=200, pool=8):
            "alg_bytes_per_step": vb + cb}
     log(f"[spec] verify {res['verify_us']:.1f} us ({res['verify_GBps']:.0f} GB/s), commit "
         f"{res['commit_us']:.1f} us ({res['commit_GBps']:.0f} GB/s)")
+    del blocks, S
+    torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(gen_inputs, w, budget_s=15.0):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(gen_inputs, w, o_dev, budget_s=15.0):
     """Oracle (float64, OpenMP) on the host cores over a bounded sample of the prefill workload:
-    the first P (sequence, head) pairs in sequence-major order, all T tokens each."""
+    the first P (sequence, head) pairs in sequence-major order, all T tokens each.  The oracle's
+    outputs for the sample are also compared with the device's outputs of the timed launches
+    (o_dev): rel-L2 and max-abs over the sample, beside the bf16 rounding floor."""
     import oracle
     import torch
     cores = oracle.default_threads()
@@ -294,26 +322,114 @@ def cpu_baseline(gen_inputs, w, budget_s=15.0):
     t1 = time.perf_counter() - t0
     # the oracle parallelises over (head, 32-column block): 4 units per head at d_v = 128
     n = int(min(len(all_pairs), max(1, budget_s / max(t1, 1e-3) * max(1, cores // 4))))
-    args, s0 = gather(all_pairs[:n])
+    pairs = all_pairs[:n]
+    args, s0 = gather(pairs)
     t0 = time.perf_counter()
-    oracle.prefill(*args, S0=s0, nthreads=cores)
+    o_ref, _ = oracle.prefill(*args, S0=s0, nthreads=cores)
     el = time.perf_counter() - t0
     token_heads = w.T * n
     tok_s = token_heads / w.H / el
     log(f"[cpu] oracle on {n} (sequence, head) pairs x {w.T} tokens: {el:.2f} s, {cores} threads")
-    del args, s0
+    # parity of the timed launches' outputs on the sample (float64 sums)
+    got = torch.stack([o_dev[b, :, h] for b, h in pairs], dim=1)[None].cpu().double()
+    y = torch.from_numpy(o_ref)
+    dif = got - y
+    fl = y.to(torch.bfloat16).double() - y
+    den = float((y * y).sum())
+    parity = {"pairs": n, "o_rel_l2": (float((dif * dif).sum()) / den) ** 0.5,
+              "o_max_abs": float(dif.abs().max()),
+              "bf16_floor_rel_l2": (float((fl * fl).sum()) / den) ** 0.5,
+              "bf16_floor_max_abs": float(fl.abs().max())}
+    log(f"[cpu] parity of the timed outputs on the sample: {parity}")
+    del args, s0, o_ref, got, y, dif, fl
     return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"first {n} of {len(all_pairs)} (sequence, head) pairs, all {w.T} tokens each "
-                      f"({token_heads} token-heads in {el:.1f} s); tokens/s = token-heads/s / {w.H}"}
+                      f"({token_heads} token-heads in {el:.1f} s); tokens/s = token-heads/s / {w.H}"}, parity
 
 
-def prefill_kernel_name() -> str:
-    """Kernel that runs the model-width workload (one 128-column slice per workgroup)."""
-    nw = 4 if os.environ.get("KDA_PREFILL_WAVES") == "4" else 8
-    pipe = os.environ.get("KDA_PREFILL_PIPE", "8")
-    if nw == 8 and pipe in ("4", "8"):
-        return f"kda_prefill_pipe_kernel<{pipe},false>"
-    return f"kda_prefill_kernel<PrefillCfg<128,{8 // nw},64,bf16,{nw}>>"
+def cpu_baseline_decode(gen, steps=10):
+    """Oracle decode steps over every state of the decode workload (256 x 56), one step at a time
+    (the state carried from step to step), timed per step."""
+    import oracle
+    w = gen.DECODE_WORKLOADS["decode_n256"]
+    cores = oracle.default_threads()
+    S = gen.make_state(w.N, w.H, w.dk, w.dv, w.s0_std, seed=w.seed, device="cpu")
+    toks = [gen.make_decode_inputs(w.N, w.H, w.dk, w.dv, w.dtype, w.decay, seed=w.seed * 10**6 + i,
+                                   device="cpu") for i in range(steps)]
+    t0 = time.perf_counter()
+    for t in toks:
+        _, S = oracle.decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], S, nthreads=cores)
+    el = time.perf_counter() - t0
+    log(f"[cpu] oracle decode: {steps} steps over {w.N} x {w.H} states: {el:.2f} s, {cores} threads")
+    return {"value": w.N * steps / el, "unit": "tokens/s", "us_per_step": el / steps * 1e6,
+            "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{steps} full steps (all {w.N * w.H} states each)"}
+
+
+def cpu_baseline_long(gen, heads=1):
+    """Oracle on `heads` of the 16 heads of the 1M-token workload, all 1,048,576 tokens, scaled to
+    the 16 heads (heads are independent and the oracle's per-head cost does not depend on h)."""
+    import oracle
+    w = gen.WORKLOADS["long_1m"]
+    cores = oracle.default_threads()
+    d = gen.workload_inputs(w, device="cpu", H=heads)
+    t0 = time.perf_counter()
+    oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"], nthreads=cores,
+                   col_block=max(1, 128 * heads // max(1, cores)))
+    el = time.perf_counter() - t0
+    full = el * w.H / heads
+    log(f"[cpu] oracle on {heads} head(s) x {w.T} tokens: {el:.2f} s ({full:.1f} s scaled to {w.H} heads)")
+    del d
+    return {"value": w.B * w.T / full, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{heads} of {w.H} heads, all {w.T} tokens ({el:.1f} s), scaled linearly to {w.H} heads"}
+
+
+def measure_peaks():
+    """Re-measured peaks on this GPU: a dense bf16 GEMM (8192^3 through torch.matmul), a read
+    stream (torch.sum over 4 GiB of fp32) and a device copy (2 GiB read + 2 GiB written)."""
+    import torch
+    res = {}
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(20):
+        c = a @ b
+    ev1.record()
+    torch.cuda.synchronize()
+    res["bf16_gemm_TFLOPs"] = 2 * 8192 ** 3 * 20 / (ev0.elapsed_time(ev1) / 1e3) / 1e12
+    del a, b, c
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        r = x.sum()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(10):
+        r = x.sum()
+    ev1.record()
+    torch.cuda.synchronize()
+    res["hbm_read_GBps"] = x.numel() * 4 * 10 / (ev0.elapsed_time(ev1) / 1e3) / 1e9
+    del r
+    y = torch.empty(1 << 29, dtype=torch.float32, device="cuda")
+    src = x[: 1 << 29]
+    for _ in range(3):
+        y.copy_(src)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(10):
+        y.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    res["hbm_copy_GBps"] = 2 * y.numel() * 4 * 10 / (ev0.elapsed_time(ev1) / 1e3) / 1e9
+    del x, y, src
+    torch.cuda.empty_cache()
+    log(f"[peaks] {res}")
+    return res
 
 
 def main():
@@ -367,7 +483,7 @@ def main():
         log(f"[decode] {step_s * 1e6:.1f} us per step, {gbs:.1f} GB/s")
         return
 
-    w, d, wall, ev, plan = bench_prefill(kda, gen, args.steps, args.warmup)
+    w, d, wall, ev, plan, o_dev = bench_prefill(kda, gen, args.steps, args.warmup)
     tokens = w.B * w.T
     tok_s = tokens * args.steps / wall
     launch_s = ev / args.steps                 # one kernel launch per step (no split)
@@ -391,7 +507,7 @@ def main():
                    "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
                    "tokens_per_step": tokens, "seg_len": plan[0], "n_vs": plan[1],
                    "parallelism": "1 GPU"},
-        "roofline": {"bound": "hbm", "kernel": prefill_kernel_name(),
+        "roofline": {"bound": "hbm", "kernel": PREFILL_KERNEL,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": profiled_value("kda_prefill_pipe_kernel_model_width.md", PREFILL_SOURCES),
@@ -408,8 +524,8 @@ def main():
     if not args.prefill_only and not args.no_gate:
         result["prefill_fused_gate"] = bench_prefill_gate(kda, gen, w, d, args.steps, args.warmup)
     if not args.prefill_only and not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d, w)
-    del d
+        result["cpu_baseline"], result["parity_sampled_vs_oracle"] = cpu_baseline(d, w, o_dev)
+    del d, o_dev
     torch.cuda.empty_cache()
 
     if not args.prefill_only and not args.no_decode:
@@ -423,6 +539,8 @@ def main():
                             "traffic": profiled_value("kda_decode_kernel_n256.md",
                                                       ["kda_decode.hip", "kda_device.h"]),
                             "tokens_per_s": wd.N * args.decode_steps / dwall}
+        if not args.no_cpu_baseline:
+            result["decode"]["cpu_baseline"] = cpu_baseline_decode(gen)
     if not args.prefill_only and not args.no_spec:
         result["spec_decode"] = bench_spec(kda, gen)
     if not args.prefill_only and not args.no_long:
@@ -436,6 +554,17 @@ def main():
                                   "automatic_plan": {"seg_len_after_first": auto_seg,
                                                      "ms_per_step": awall / nsteps * 1e3,
                                                      "tokens_per_s": wl.B * wl.T * nsteps / awall}}
+        if not args.no_cpu_baseline:
+            result["long_context"]["cpu_baseline"] = cpu_baseline_long(gen)
+    if not args.prefill_only:
+        peaks = measure_peaks()
+        rf = result["roofline"]
+        rf["peak_measured"] = {"hbm_read_GBps": peaks["hbm_read_GBps"], "hbm_copy_GBps": peaks["hbm_copy_GBps"],
+                               "bf16_gemm_TFLOPs": peaks["bf16_gemm_TFLOPs"]}
+        rf["frac_of_measured_read"] = rf["achieved"] / peaks["hbm_read_GBps"]
+        rf["useful_frac_of_measured_gemm"] = rf["useful_tflops"] / peaks["bf16_gemm_TFLOPs"]
+        if "decode" in result:
+            result["decode"]["frac_of_measured_copy"] = result["decode"]["state_GBps"] / peaks["hbm_copy_GBps"]
     print(json.dumps(result), flush=True)
 
 

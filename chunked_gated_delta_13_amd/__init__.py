@@ -17,7 +17,8 @@ import ctypes
 from . import _lib
 from ._lib import KDAError
 
-__all__ = ["chunk_prefill", "decode_step", "prefill_plan", "prefill_workspace_bytes",
+__all__ = ["chunk_prefill", "chunk_prefill_ckpt", "chunk_prefill_gate",
+           "decode_step", "spec_verify", "spec_commit", "prefill_plan", "prefill_workspace_bytes",
            "abi_version", "KDAError", "load_library"]
 
 
@@ -71,9 +72,14 @@ def prefill_plan(B, T, H, dk, dv, chunk=64, dtype=None):
 
 
 def prefill_workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=None, seg_len=0):
+    """Device workspace bytes of a prefill on the automatic plan (seg_len 0) or with explicit
+    segments of seg_len tokens."""
     torch = _torch()
     code = _dtype_code(dtype or torch.bfloat16)
-    return int(_lib.load().kda_chunk_prefill_workspace_bytes(B, T, H, dk, dv, chunk, code, seg_len))
+    lib = _lib.load()
+    if seg_len == 0:
+        return int(lib.kda_chunk_prefill_workspace_bytes(B, T, H, dk, dv, chunk, code))
+    return int(lib.kda_chunk_prefill_workspace_bytes_ex(B, T, H, dk, dv, chunk, code, seg_len))
 
 
 def chunk_prefill(q, k, v, log_alpha, beta, S0=None, chunk=64, *, seg_len=0, n_vs=0,
@@ -127,7 +133,7 @@ def _prefill(q, k, v, log_alpha, beta, S0, chunk, seg_len, n_vs, o, S_T, return_
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     elif S_T is not None:
         _check_tensor("S_T", S_T, torch.float32, (B, H, dk, dv), dev)
-    need = int(lib.kda_chunk_prefill_workspace_bytes(B, T, H, dk, dv, chunk, code, seg_len))
+    need = prefill_workspace_bytes(B, T, H, dk, dv, chunk, q.dtype, seg_len)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -204,7 +210,7 @@ def chunk_prefill_gate(q, k, v, gate, beta, S0=None, chunk=64, *, seg_len=0, n_v
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     elif S_T is not None:
         _check_tensor("S_T", S_T, torch.float32, (B, H, dk, dv), dev)
-    need = int(lib.kda_chunk_prefill_workspace_bytes(B, T, H, dk, dv, chunk, code, seg_len))
+    need = prefill_workspace_bytes(B, T, H, dk, dv, chunk, q.dtype, seg_len)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -31,7 +31,8 @@ SIGNATURES = {
     "kda_status_string": (ctypes.c_char_p, [_i]),
     "kda_chunk_prefill_plan": (_i, [_i, _i, _i, _i, _i, _i, _i,
                                     ctypes.POINTER(_i), ctypes.POINTER(_i)]),
-    "kda_chunk_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "kda_chunk_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "kda_chunk_prefill_workspace_bytes_ex": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "kda_chunk_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "kda_chunk_prefill_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,

@@ -34,9 +34,8 @@ long long min_segment(long long T) {
     const long long l = (long long)(8.0 * sqrt((double)T));
     return l > 512 ? l : 512;
 }
-constexpr int kDefaultWaves = 8;            // waves per workgroup for 128-column bf16 slices
-constexpr int kDefaultPipeChunkWaves = 8;   // chunk waves of the two-role prefill kernel
-constexpr int kDualChunk = 64;              // longest chunk of the shared transition/increment pass
+constexpr int kSliceWaves = 8;        // waves per workgroup for 128-column bf16 slices
+constexpr int kPipeChunkWaves = 8;    // chunk waves of the two-role prefill kernel
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -107,6 +106,12 @@ int cu_count() {
     return cached[dev];
 }
 
+// Chunk length the kernels run for a caller's chunk.  fp32 operands of a 64-token chunk do not fit
+// the 160 KiB of LDS of one workgroup, so an fp32 call with chunk 64 runs as 32-token chunks: the
+// result of the method does not depend on the chunk length beyond rounding, and every length the
+// caller may pass with chunk 64 (segment length, checkpoint spacing) is a multiple of 32.
+int kernel_chunk(int chunk, kda_dtype_t dt) { return (dt == KDA_F32 && chunk == 64) ? 32 : chunk; }
+
 // Shape checks shared by the prefill entry points.
 kda_status_t check_prefill_shape(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt) {
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARGUMENT;
@@ -114,7 +119,7 @@ kda_status_t check_prefill_shape(int B, int T, int H, int dk, int dv, int chunk,
     if (dk <= 0 || dv <= 0 || chunk <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
     if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
-    if (!kda::prefill_supported(dk, dv, chunk, dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
+    if (!kda::prefill_supported(dk, dv, kernel_chunk(chunk, dt), dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
     long long n = 0;
     if (!mul_ok((long long)B * T, (long long)H * dk, &n)) return KDA_ERR_INVALID_ARGUMENT;
     // lane offsets inside one chunk are 32-bit byte offsets: 64 token rows of H * dk fp32 values
@@ -204,10 +209,6 @@ void auto_plan(int B, int T, int H, int dk, int dv, int chunk, bool f32, int* se
     if (units > 0 && 2 * units <= cus && (long long)T >= 3 * lmin) {
         long long m = (cus - 1) / units;   // segments after the first
         if (m > T / lmin - 1) m = T / lmin - 1;
-        if (const char* e = getenv("KDA_SPLIT_MAX")) {   // tuning only: cap on m
-            const long long v = atoll(e);
-            if (v >= 2 && v < m) m = v;
-        }
         if (m >= 2) {
             const double r = kda::prefill_dual_supported(dk, dv / vs, chunk, f32) ? kSharedPassCost : kTwoPassCost;
             // L: the nearest multiple of the chunk; segment 0 takes what the others leave (if
@@ -229,15 +230,16 @@ void auto_plan(int B, int T, int H, int dk, int dv, int chunk, bool f32, int* se
 kda_status_t resolve_plan(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt,
                           int seg_len_in, int n_vs_in, long long* seg_len, int* n_seg, int* n_vs,
                           long long* shift) {
+    if (seg_len_in < 0 || (seg_len_in > 0 && seg_len_in % chunk != 0)) return KDA_ERR_INVALID_ARGUMENT;
+    // segment lengths are whole chunks of the caller's length (multiples of the kernels' chunk too)
     int a_seg = 0, a_vs = 0;
     long long a_sh = 0;
     auto_plan(B, T, H, dk, dv, chunk, dt == KDA_F32, &a_seg, &a_vs, &a_sh);
     long long sl = seg_len_in > 0 ? seg_len_in : a_seg;
     long long sh = seg_len_in > 0 ? 0 : a_sh;
-    if (seg_len_in < 0 || (seg_len_in > 0 && seg_len_in % chunk != 0)) return KDA_ERR_INVALID_ARGUMENT;
     int vs = n_vs_in > 0 ? n_vs_in : a_vs;
     if (n_vs_in < 0 || vs > 2 || (vs == 2 && dv != 128)) return KDA_ERR_INVALID_ARGUMENT;
-    if (!kda::prefill_supported(dk, dv / vs, chunk, dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
+    if (!kda::prefill_supported(dk, dv / vs, kernel_chunk(chunk, dt), dt == KDA_F32)) return KDA_ERR_UNSUPPORTED;
     if (sl <= 0 || sl + sh >= T) {
         sl = T > 0 ? T : chunk;
         sh = 0;
@@ -273,36 +275,23 @@ bool prefill_supported(int dk, int dvw, int chunk, bool f32) {
     if (dvw != 64 && dvw != 128) return false;
     if (dvw > dk) return false;
     if (chunk != 16 && chunk != 32 && chunk != 64) return false;
-    if (f32 && chunk == 64) return false;   // fp32 operands for a 64-token chunk exceed 160 KiB of LDS
+    if (f32 && chunk == 64) return false;   // fp32 operands of a 64-token chunk exceed 160 KiB of LDS
     return true;
 }
 
-// Waves per workgroup for a 128-column slice in bf16: 4 (32 columns per wave) or 8 (16 columns
-// per wave, two waves per SIMD).  KDA_PREFILL_WAVES overrides the default (tuning only).
+// Waves per workgroup of the single-role kernel: 8 for a 128-column bf16 slice at d_k = 128 (16
+// columns per wave, two waves per SIMD), else 4.
 int prefill_waves(int dk, int dvw, bool f32) {
     if (f32 || dk != 128 || dvw != 128) return 4;
-    static int cached = 0;
-    if (cached == 0) {
-        const char* e = getenv("KDA_PREFILL_WAVES");
-        cached = (e && atoi(e) == 8) ? 8 : (e && atoi(e) == 4) ? 4 : kDefaultWaves;
-    }
-    return cached;
+    return kSliceWaves;
 }
 
-// Chunk waves of the two-role look-ahead kernel (4 or 8), or 0 when a launch does not run on it.
-// It takes bf16, d_k = d_v = 128 in one slice, 64-token chunks, no per-sequence lengths and real
-// values.  KDA_PREFILL_PIPE=0 keeps such launches on the single-role kernel and
-// KDA_PREFILL_PIPE=4 or 8 picks the chunk waves (tuning and cross-checks only).
+// Chunk waves of the two-role look-ahead kernel, or 0 when a launch does not run on it.  It takes
+// bf16, d_k = d_v = 128 in one slice, 64-token chunks, no per-sequence lengths and real values.
 static int pipe_chunk_waves(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a) {
-    static int ncw = -1;
-    if (ncw < 0) {
-        const char* e = getenv("KDA_PREFILL_PIPE");
-        const int v = e ? atoi(e) : kDefaultPipeChunkWaves;
-        ncw = (v == 0 || v == 4 || v == 8) ? v : kDefaultPipeChunkWaves;
-    }
     const bool fits = !f32 && dk == 128 && dvw == 128 && chunk == 64 && a.n_vs == 1 && !a.lens &&
                       !a.zero_values && prefill_waves(dk, dvw, f32) == 8;
-    return fits ? ncw : 0;
+    return fits ? kPipeChunkWaves : 0;
 }
 
 hipError_t launch_prefill(int dk, int dvw, int chunk, bool f32, const PrefillArgs& a, hipStream_t s) {
@@ -353,8 +342,12 @@ kda_status_t kda_chunk_prefill_plan(int B, int T, int H, int dk, int dv, int chu
     return KDA_OK;
 }
 
-size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt,
-                                         int seg_len) {
+size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt) {
+    return kda_chunk_prefill_workspace_bytes_ex(B, T, H, dk, dv, chunk, dt, 0);
+}
+
+size_t kda_chunk_prefill_workspace_bytes_ex(int B, int T, int H, int dk, int dv, int chunk, kda_dtype_t dt,
+                                            int seg_len) {
     if (check_prefill_shape(B, T, H, dk, dv, chunk, dt) != KDA_OK) return 0;
     long long sl = 0;
     int ns = 0, vs = 0;
@@ -411,6 +404,7 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     st = resolve_plan(B, T, H, dk, dv, chunk, dt, seg_len, n_vs, &sl, &ns, &vs, &shift);
     if (st != KDA_OK) return st;
     if (B == 0 || H == 0) return KDA_OK;
+    chunk = kernel_chunk(chunk, dt);
 
     const size_t esz = dt == KDA_BF16 ? 2 : 4;
     const size_t ntok = (size_t)B * T * H;
@@ -554,15 +548,9 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     pm.seg0 = 1;
     pm.n_seg_launch = ns - 2;
     pm.n_units = (int)(bh * (ns - 2));
-    // The shared transition/increment pass may use another chunk than the output pass (M_s and
-    // H_s do not depend on it beyond rounding).  It uses the caller's chunk: at 64 tokens the two
-    // states spill a few registers outside the chunk loop, and the pass is still faster than at
-    // 32.  KDA_DUAL_CHUNK overrides (tuning only).
-    int dchunk = chunk > kDualChunk ? kDualChunk : chunk;
-    if (const char* e = getenv("KDA_DUAL_CHUNK")) {
-        const int v = atoi(e);
-        if ((v == 16 || v == 32 || v == 64) && sl % v == 0 && shift % v == 0) dchunk = v;
-    }
+    // The shared transition/increment pass runs the caller's chunk (at 64 tokens the two states
+    // spill a few registers outside the chunk loop, and the pass is still faster than at 32).
+    const int dchunk = chunk;
 
     {
         // segment 0 overlaps the transition/increment pass on a side stream: fork after the
@@ -652,9 +640,13 @@ kda_status_t kda_spec_verify(const void* q, const void* k, const void* v, const 
     if (N < 0 || H < 0 || m < 1) return KDA_ERR_INVALID_ARGUMENT;
     if (N > 0 && H > 0 && !S) return KDA_ERR_INVALID_ARGUMENT;
     if (m > kSpecTokenLoopMax) {
-        // a long block runs from S as one short chunked prefill; no state is written
-        return kda_chunk_prefill_ex(q, k, v, log_alpha, beta, S, o, nullptr, N, m, H, dk, dv, spec_chunk(m, dt),
-                                    dt, 0, 0, nullptr, 0, stream);
+        // a long block runs from S as one unsplit chunked prefill (one segment as long as the block,
+        // so no workspace is needed); no state is written
+        const int sc = spec_chunk(m, dt);
+        const long long whole = ((long long)m + sc - 1) / sc * sc;
+        if (whole > 0x7fffffffLL) return KDA_ERR_UNSUPPORTED;
+        return kda_chunk_prefill_ex(q, k, v, log_alpha, beta, S, o, nullptr, N, m, H, dk, dv, sc, dt, (int)whole,
+                                    0, nullptr, 0, stream);
     }
     const kda_status_t st = check_spec_pointers(q, k, v, log_alpha, beta, S, o, nullptr, N, m, H, dk, dv, dt);
     if (st != KDA_OK || N == 0 || H == 0) return st;
@@ -708,11 +700,14 @@ kda_status_t kda_spec_commit(const void* q, const void* k, const void* v, const 
     const int chunk = spec_chunk(m, dt);
     kda_status_t st = check_prefill_shape(N, m, H, dk, dv, chunk, dt);
     if (st != KDA_OK) return st;
+    // one segment as long as the block: the commit never splits the sequence
+    const long long whole = ((long long)m + chunk - 1) / chunk * chunk;
+    if (whole > 0x7fffffffLL) return KDA_ERR_UNSUPPORTED;
     long long sl = 0;
     int ns = 0, vs = 0;
-    st = resolve_plan(N, m, H, dk, dv, chunk, dt, 0, 0, &sl, &ns, &vs, nullptr);
+    st = resolve_plan(N, m, H, dk, dv, chunk, dt, (int)whole, 0, &sl, &ns, &vs, nullptr);
     if (st != KDA_OK) return st;
-    if (ns != 1) return KDA_ERR_UNSUPPORTED;
+    if (ns != 1) return KDA_ERR_UNSUPPORTED;   // unreachable: seg_len >= m
     if (N == 0 || H == 0) return KDA_OK;
     if (!q || !k || !v || !log_alpha || !beta || !S || !accepted) return KDA_ERR_INVALID_ARGUMENT;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(log_alpha, 16) || !aligned(S, 16) ||

@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "../../include/kda.h"
+
 namespace kda {
 
 // One launch of the fused chunk kernel over units (b, h, segment, column slice).
@@ -96,5 +98,6 @@ hipError_t launch_scan(int dk, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_decode(int dk, bool f32, const DecodeArgs& a, hipStream_t stream);
 // dst[i] = src ? src[i] : 0 for n floats
 hipError_t launch_state_copy(float* dst, const float* src, long long n, hipStream_t stream);
+
 
 }  // namespace kda

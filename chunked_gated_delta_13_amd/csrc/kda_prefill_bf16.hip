@@ -1,15 +1,11 @@
-// bf16-input instantiations of the fused chunk-prefill kernel.
+// bf16-input instantiations of the fused chunk-prefill kernel: a 128-column slice at d_k = 128 runs
+// on 8 waves (16 columns each), every other slice on 4.
 #include "kda_prefill_kernel.h"
 
 namespace kda {
 
 hipError_t launch_prefill_bf16(int dk, int dvw, int nw, int chunk, const PrefillArgs& a, hipStream_t s) {
     using T = __bf16;
-    if (dk == 128 && dvw == 128 && nw == 4) {
-        if (chunk == 64) return launch_prefill_cfg<PrefillCfg<128, 2, 64, T, 4>>(a, s);
-        if (chunk == 32) return launch_prefill_cfg<PrefillCfg<128, 2, 32, T, 4>>(a, s);
-        if (chunk == 16) return launch_prefill_cfg<PrefillCfg<128, 2, 16, T, 4>>(a, s);
-    }
     if (dk == 128 && dvw == 128 && nw == 8) {
         if (chunk == 64) return launch_prefill_cfg<PrefillCfg<128, 1, 64, T, 8>>(a, s);
         if (chunk == 32) return launch_prefill_cfg<PrefillCfg<128, 1, 32, T, 8>>(a, s);

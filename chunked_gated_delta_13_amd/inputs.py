@@ -160,6 +160,34 @@ def make_prefill_inputs(B, T, H, dk, dv, dtype="bf16", decay="sig2", s0_std=0.02
     return {"q": q, "k": k, "v": v, "log_alpha": la, "beta": beta, "S0": S0}
 
 
+def make_stress_inputs(B, T, H, d, dtype="bf16", seed=0, beta_lo=0.0, beta_hi=2.0, group=16,
+                       noise=0.05, decay="slow", s0_std=1.0, device="cpu"):
+    """Inputs that stress the intra-chunk triangular solve: the keys of every `group`
+    consecutive tokens (per sequence and head) are near-parallel, each the unit vector of
+    u + noise * z with one shared u ~ N(0, I) per group and z ~ N(0, I / d) per token (cosine of
+    two keys of a group about 1 - noise^2), and beta ~ U[beta_lo, beta_hi].  With unit keys and
+    beta in [0, 2] every token's transition is still a contraction, but the unit lower-triangular
+    system of a chunk then has off-diagonal entries near beta, far from the identity.
+    Drawn in the order q, u, z, v, beta, log_alpha, S0; the rest as make_prefill_inputs."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    dt = torch_dtype(dtype)
+    q = _unit_rows(_normal((B, T, H, d), gen, device)).to(dt).contiguous()
+    ng = (T + group - 1) // group
+    u = _normal((B, ng, H, d), gen, device)
+    u = u / torch.linalg.vector_norm(u, dim=-1, keepdim=True).clamp_min(1e-30)
+    z = _normal((B, T, H, d), gen, device) / (d ** 0.5)
+    base = u.repeat_interleave(group, dim=1)[:, :T]
+    k = _unit_rows(base + noise * z).to(dt).contiguous()
+    v = _normal((B, T, H, d), gen, device).to(dt).contiguous()
+    beta = (beta_lo + (beta_hi - beta_lo) * torch.rand((B, T, H), generator=gen, device=device)).contiguous()
+    la = _log_alpha((B, T, H), d, decay, 0.0, gen, device)
+    S0 = None
+    if s0_std > 0.0:
+        S0 = (s0_std * _normal((B, H, d, d), gen, device)).contiguous()
+    return {"q": q, "k": k, "v": v, "log_alpha": la, "beta": beta, "S0": S0}
+
+
 def workload_inputs(w: PrefillWorkload, device="cpu", T: int | None = None,
                     B: int | None = None, H: int | None = None):
     """Inputs of a named workload, optionally with a smaller B, T or H (same recipe)."""

@@ -80,12 +80,20 @@ kda_status_t kda_chunk_prefill_plan(int B, int T, int H, int dk, int dv, int chu
                                     kda_dtype_t dtype, int *seg_len, int *n_vs);
 
 /*
- * Bytes of device workspace that kda_chunk_prefill_ex needs for `seg_len`
- * (0 = the automatic plan).  0 when the sequence is not split.  Returns 0 for
- * shapes that kda_chunk_prefill would reject.
+ * Bytes of device workspace that kda_chunk_prefill needs (the automatic plan):
+ * the per-segment transitions and increments and the segments' entry states of
+ * a sequence split, 0 when the sequence is not split.  Returns 0 for shapes
+ * that kda_chunk_prefill would reject.
  */
 size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
-                                         kda_dtype_t dtype, int seg_len);
+                                         kda_dtype_t dtype);
+
+/*
+ * kda_chunk_prefill_workspace_bytes for an explicit segment length `seg_len`
+ * (0 = the automatic plan), as passed to kda_chunk_prefill_ex.
+ */
+size_t kda_chunk_prefill_workspace_bytes_ex(int B, int T, int H, int dk, int dv, int chunk,
+                                            kda_dtype_t dtype, int seg_len);
 
 /*
  * Chunked KDA prefill over T tokens from the initial state S0.
@@ -103,10 +111,11 @@ size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, in
  *   S_T        [B, H, dk, dv] fp32 or NULL   final state (NULL = not written);
  *                                            may be exactly S0 (in place), must not
  *                                            partially overlap it
- *   chunk      16, 32 or 64 tokens per chunk (64 only for KDA_BF16); the result
- *              does not depend on it beyond rounding
+ *   chunk      16, 32 or 64 tokens per chunk; the result does not depend on it
+ *              beyond rounding.  KDA_F32 with chunk 64 runs as 32-token chunks
+ *              (fp32 operands of a 64-token chunk exceed the LDS of one workgroup)
  *   dk == dv   64 or 128
- *   workspace  device scratch of at least kda_chunk_prefill_workspace_bytes(...,0)
+ *   workspace  device scratch of at least kda_chunk_prefill_workspace_bytes(...)
  *              bytes (may be NULL when that is 0)
  * T == 0 is valid: S_T receives S0 (or zeros).  B == 0 or H == 0 is a no-op.
  */
@@ -134,7 +143,7 @@ kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v,
  * Pages: "Kimi K3's architecture", "The bill comes due in the serving stack"
  * (per segment, the transition and the state reached from zero combine
  * exactly across segments).
- * The workspace must hold kda_chunk_prefill_workspace_bytes(..., seg_len).
+ * The workspace must hold kda_chunk_prefill_workspace_bytes_ex(..., seg_len).
  */
 kda_status_t kda_chunk_prefill_ex(const void *q, const void *k, const void *v,
                                   const float *log_alpha, const float *beta, const float *S0,
@@ -212,7 +221,8 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
  * K3's architecture" (orkas.ai), "The bill comes due in the serving stack" (the state is
  * updated in place, so a rejected draft cannot be undone; the projected inputs are kept and
  * the state is rebuilt on chip).  Blocks of up to 16 tokens run as a token loop with the state
- * held on chip (read once); longer blocks run as one short chunked prefill (chunk 32 or 64).
+ * held on chip (read once); longer blocks, of any length m, run as one unsplit chunked prefill
+ * over the block (chunk 32 or 64, one workgroup per sequence and head; no workspace needed).
  *
  *   q, k       [N, m, H, dk]  dtype          drafted queries, keys
  *   v          [N, m, H, dv]  dtype
@@ -239,6 +249,8 @@ kda_status_t kda_spec_verify(const void *q, const void *k, const void *v,
  *   accepted   [N]            int32 DEVICE   tokens to keep per sequence; values outside
  *                                            [0, m] are clamped on the device (0 leaves S as is)
  * No output rows are written.  S must not overlap any input.  N == 0 or H == 0 is a no-op.
+ * Blocks longer than 16 tokens, of any length m, run as one unsplit chunked prefill with
+ * per-sequence lengths (no workspace needed).
  */
 kda_status_t kda_spec_commit(const void *q, const void *k, const void *v,
                              const float *log_alpha, const float *beta, float *S,

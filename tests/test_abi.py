@@ -20,7 +20,7 @@ from chunked_gated_delta_13_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+OK, INVALID, UNSUPPORTED, WORKSPACE, DEVICE = 0, 1, 2, 3, 4
 BF16, F32 = 0, 1
 
 
@@ -96,7 +96,6 @@ def _ok_ptrs():
     (dict(dk=96, dv=96), UNSUPPORTED),
     (dict(dk=128, dv=64), UNSUPPORTED),
     (dict(chunk=48), UNSUPPORTED),
-    (dict(chunk=64, dt=F32), UNSUPPORTED),
     (dict(B=-1), INVALID),
     (dict(T=-5), INVALID),
     (dict(H=-2), INVALID),
@@ -139,7 +138,7 @@ def test_prefill_overlaps(lib, host_only):
 
 def test_prefill_workspace_required(lib, host_only):
     args = _ok_ptrs()
-    need = lib.kda_chunk_prefill_workspace_bytes(1, 8192, 2, 128, 128, 64, BF16, 2048)
+    need = lib.kda_chunk_prefill_workspace_bytes_ex(1, 8192, 2, 128, 128, 64, BF16, 2048)
     assert need == 2 * (3 * 2 * 128 * 128 + 4 * 128 * 128) * 4
     assert _prefill(lib, T=8192, seg=2048, **args) == WORKSPACE
     assert _prefill(lib, T=8192, seg=2048, ws=_ptrs(7), ws_bytes=need - 4, **args) == WORKSPACE
@@ -187,7 +186,7 @@ def test_plan_rules(lib):
     assert lib.kda_chunk_prefill_plan(1, 1500, 1, 128, 128, 64, BF16, ctypes.byref(seg),
                                       ctypes.byref(nvs)) == OK
     assert seg.value == 1500
-    assert lib.kda_chunk_prefill_workspace_bytes(1, 1500, 1, 128, 128, 64, BF16, 0) == 0
+    assert lib.kda_chunk_prefill_workspace_bytes(1, 1500, 1, 128, 128, 64, BF16) == 0
     # a few thousand tokens on one head: segments of at least the minimum length
     assert lib.kda_chunk_prefill_plan(1, 6000, 1, 128, 128, 64, BF16, ctypes.byref(seg),
                                       ctypes.byref(nvs)) == OK
@@ -205,16 +204,16 @@ def test_automatic_plan_properties(lib):
     import math
     seg = ctypes.c_int(0)
     nvs = ctypes.c_int(0)
-    lib.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
     checked = 0
     for B, H, T, d, (dt, chunk) in itertools.product(
             (1, 2, 4), (1, 2, 8, 16, 56), (1, 100, 1000, 1536, 4096, 6000, 12288, 65536, 1 << 20),
-            (64, 128), ((BF16, 64), (BF16, 32), (F32, 16), (F32, 32))):
+            (64, 128), ((BF16, 64), (BF16, 32), (F32, 16), (F32, 32), (F32, 64))):
         assert lib.kda_chunk_prefill_plan(B, T, H, d, d, chunk, dt, ctypes.byref(seg),
                                           ctypes.byref(nvs)) == OK
         L, vs = seg.value, nvs.value
         units = B * H * vs
-        ws = lib.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, chunk, dt, 0)
+        ws = lib.kda_chunk_prefill_workspace_bytes(B, T, H, d, d, chunk, dt)
+        assert ws == lib.kda_chunk_prefill_workspace_bytes_ex(B, T, H, d, d, chunk, dt, 0)
         lmin = max(512, 8 * math.sqrt(T))
         if L >= T:   # no split
             assert ws == 0
@@ -304,3 +303,37 @@ def test_gate_validation(lib, host_only):
     assert _gate(lib, nvs=2) == UNSUPPORTED
     assert _gate(lib, gate=None) == INVALID
     assert _gate(lib, gate=_ptrs(3) + 2) == INVALID
+
+
+def test_fp32_chunk64_is_supported(lib):
+    """fp32 inputs take every chunk length, 64 included (run as 32-token chunks inside the
+    library): the plan and the workspace query accept it, segment lengths are whole 64-token
+    chunks, and an explicit segment length must be a multiple of 64."""
+    seg = ctypes.c_int(0)
+    nvs = ctypes.c_int(0)
+    for d in (64, 128):
+        assert lib.kda_chunk_prefill_plan(1, 1 << 16, 2, d, d, 64, F32, ctypes.byref(seg),
+                                          ctypes.byref(nvs)) == OK
+        assert seg.value % 64 == 0 and seg.value < (1 << 16)
+        assert lib.kda_chunk_prefill_workspace_bytes(1, 1 << 16, 2, d, d, 64, F32) > 0
+        assert lib.kda_chunk_prefill_workspace_bytes_ex(1, 4096, 2, d, d, 64, F32, 1024) == \
+            2 * (3 * 2 * d * d + 4 * d * d) * 4
+    args = _ok_ptrs()
+    assert _prefill(lib, dt=F32, chunk=64, seg=96, **args) == INVALID   # not a multiple of 64
+
+
+def test_spec_long_block_never_needs_workspace(lib, host_only):
+    """A drafted block longer than 16 tokens runs as one unsplit chunked prefill, so no length
+    asks for a workspace, even where the automatic plan would split a prefill of that many
+    tokens (1 sequence, 1 head, 2048 tokens).  Without a GPU the valid call gets as far as the
+    launch (KDA_ERR_DEVICE); it never reports a missing workspace or an unsupported length."""
+    seg = ctypes.c_int(0)
+    nvs = ctypes.c_int(0)
+    assert lib.kda_chunk_prefill_plan(1, 2048, 1, 128, 128, 64, BF16, ctypes.byref(seg),
+                                      ctypes.byref(nvs)) == OK
+    assert seg.value < 2048   # the same shape as a prefill would be split
+    for fn in ("kda_spec_verify", "kda_spec_commit"):
+        for m, dt in ((2048, BF16), (2048, F32), (40, BF16), (100000, BF16)):
+            st = _spec(lib, fn, N=1, m=m, H=1, dt=dt)
+            assert st in (OK, DEVICE), (fn, m, dt, st)
+

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from chunked_gated_delta_13_amd import inputs as gen
-from tests.parity import assert_close, to_device, to_f64
+from tests.parity import assert_close, nan_like, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -28,14 +28,17 @@ def _kda():
     ("f32", 64, 300, 16, 32, 0),
     ("bf16", 128, 512, 64, 512, 0),        # one checkpoint, at the last token
     ("bf16", 128, 12288, 64, 4096, 0),     # automatic split: segments 4480 + 3904 + 3904 tokens
+    ("f32", 128, 700, 64, 128, 0),         # fp32 with 64-token chunks
 ])
 def test_prefill_checkpoints_match_oracle(dtype, d, T, chunk, every, seg):
     kda = _kda()
     print(f"ckpt dtype={dtype} d={d} T={T} chunk={chunk} every={every} seg={seg}", flush=True)
     inp = gen.make_prefill_inputs(2, T, 2, d, d, dtype, "slow", 1.0, 90 + T, 0.0, "cpu")
     dd = to_device(inp)
+    ck0 = torch.full((2, T // every, 2, d, d), float("nan"), dtype=torch.float32, device="cuda")
     o, st, ck = kda.chunk_prefill_ckpt(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], dd["S0"],
-                                       chunk=chunk, ckpt_every=every, seg_len=seg)
+                                       chunk=chunk, ckpt_every=every, seg_len=seg, o=nan_like(dd["v"]),
+                                       S_T=nan_like(dd["S0"]), S_ckpt=ck0)
     torch.cuda.synchronize()
     o_ref, s_ref, ck_ref = oracle.prefill_ckpt(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
                                                inp["S0"], every)

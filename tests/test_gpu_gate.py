@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from chunked_gated_delta_13_amd import inputs as gen
-from tests.parity import assert_close, to_device
+from tests.parity import assert_close, nan_like, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def test_prefill_gate_matches_oracle(B, T, chunk, seg, decay):
         g = (g.float() - 8.0).to(torch.bfloat16)    # long memory: sigmoid(x) small
     dd = to_device(inp)
     o, st = kda.chunk_prefill_gate(dd["q"], dd["k"], dd["v"], g.cuda(), dd["beta"], dd["S0"], chunk=chunk,
-                                   seg_len=seg)
+                                   seg_len=seg, o=nan_like(dd["v"]), S_T=nan_like(dd["S0"]))
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.prefill_gate(inp["q"], inp["k"], inp["v"], g, inp["beta"], inp["S0"])
     assert_close("o", o, o_ref, "bf16")

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from chunked_gated_delta_13_amd import inputs as gen
-from tests.parity import assert_close, to_device
+from tests.parity import assert_close, nan_like, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def test_spec_verify_matches_oracle_and_keeps_state(dtype, d, m):
     inp = _case(6, m, 2, d, dtype, seed=40 + m)
     dd = to_device(inp)
     S = dd["S0"].clone()
-    o = kda.spec_verify(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], S)
+    o = kda.spec_verify(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], S, o=nan_like(dd["v"]))
     torch.cuda.synchronize()
     assert torch.equal(S, dd["S0"])
     o_ref = oracle.spec_verify(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
@@ -48,7 +48,8 @@ def test_spec_verify_matches_oracle_and_keeps_state(dtype, d, m):
 
 @pytest.mark.parametrize("dtype,d,m", [("bf16", 128, 4), ("bf16", 128, 2), ("bf16", 64, 3),
                                        ("f32", 128, 4), ("f32", 64, 2), ("bf16", 128, 16),
-                                       ("bf16", 64, 33), ("f32", 64, 5), ("f32", 128, 17)])
+                                       ("bf16", 64, 33), ("f32", 64, 5), ("f32", 128, 17),
+                                       ("bf16", 128, 40), ("bf16", 128, 64)])
 def test_spec_commit_matches_oracle(dtype, d, m):
     kda = _kda()
     print(f"spec commit dtype={dtype} d={d} m={m}", flush=True)
@@ -110,3 +111,25 @@ def test_spec_verify_commit_continue_matches_decode_chain():
                               inp["log_alpha"][:, :a + m], inp["beta"][:, :a + m], inp["S0"])
     assert_close("o accepted", o1[:, :a], o_ref[:, :a], "bf16")
     assert_close("o continued", o2, o_ref[:, a:a + m], "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_spec_long_block_runs_unsplit(dtype):
+    """A 2048-token drafted block of one sequence and one head: a prefill of that shape would be
+    split by the automatic plan, but verify and commit run it as one unsplit chunked prefill with
+    no workspace, and match the oracle."""
+    kda = _kda()
+    m = 2048
+    assert kda.prefill_plan(1, m, 1, 128, 128, 64)[0] < m
+    inp = _case(1, m, 1, 128, dtype, seed=95, decay="slow")
+    dd = to_device(inp)
+    S = dd["S0"].clone()
+    o = kda.spec_verify(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], S, o=nan_like(dd["v"]))
+    acc = torch.tensor([m - 100], dtype=torch.int32, device="cuda")
+    kda.spec_commit(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], S, acc)
+    torch.cuda.synchronize()
+    o_ref = oracle.spec_verify(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
+    S_ref = oracle.spec_commit(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"],
+                               acc.cpu().numpy())
+    assert_close("o", o, o_ref, dtype)
+    assert_close("S", S, S_ref, dtype)
