@@ -17,7 +17,7 @@ import ctypes
 from . import _lib
 from ._lib import KDAError
 
-__all__ = ["chunk_prefill", "chunk_prefill_ckpt", "chunk_prefill_gate",
+__all__ = ["chunk_prefill", "chunk_prefill_ckpt", "chunk_prefill_gate", "chunk_prefill_noalloc",
            "decode_step", "spec_verify", "spec_commit", "prefill_plan", "prefill_workspace_bytes",
            "abi_version", "KDAError", "load_library"]
 
@@ -219,6 +219,39 @@ def chunk_prefill_gate(q, k, v, gate, beta, S0=None, chunk=64, *, seg_len=0, n_v
                                     _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, code, seg_len, n_vs,
                                     _ptr(workspace), ws_bytes, ctypes.c_void_p(stream))
     _lib.check(st, "kda_chunk_prefill_gate")
+    return o, S_T
+
+
+def chunk_prefill_noalloc(q, k, v, log_alpha, beta, S0=None, chunk=64, *, seg_len=0, n_vs=0, o,
+                          S_T=None):
+    """chunk_prefill through the allocation-free entry point: the caller passes the output
+    tensors (o, and S_T or None), and a sequence split takes its scratch from the library's
+    fixed device array instead of a workspace.  Allocates nothing.  Returns (o, S_T)."""
+    torch = _torch()
+    lib = _lib.load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_prefill_noalloc runs on a HIP device; got a tensor on " + str(dev))
+    code = _dtype_code(q.dtype)
+    _check_tensor("q", q, q.dtype, (B, T, H, dk), dev)
+    _check_tensor("k", k, q.dtype, (B, T, H, dk), dev)
+    _check_tensor("v", v, q.dtype, (B, T, H, dv), dev)
+    _check_tensor("log_alpha", log_alpha, torch.float32, (B, T, H, dk), dev)
+    _check_tensor("beta", beta, torch.float32, (B, T, H), dev)
+    _check_tensor("o", o, q.dtype, (B, T, H, dv), dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, torch.float32, (B, H, dk, dv), dev)
+    if S_T is not None:
+        _check_tensor("S_T", S_T, torch.float32, (B, H, dk, dv), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.kda_chunk_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                       _ptr(S0), _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, code,
+                                       seg_len, n_vs, ctypes.c_void_p(stream))
+    _lib.check(st, "kda_chunk_prefill_noalloc")
     return o, S_T
 
 

@@ -22,6 +22,9 @@ KDA_ERR_DEVICE = 4
 KDA_BF16 = 0
 KDA_F32 = 1
 
+# bytes of the device array behind kda_chunk_prefill_noalloc (KDA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
 # name -> (restype, argtypes); mirrors include/kda.h
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -41,6 +44,8 @@ SIGNATURES = {
                                     _i, _i, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _vp, _sz, _vp]),
     "kda_chunk_prefill_gate": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "kda_chunk_prefill_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "kda_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _i, _i, _i, _i, _i, _vp]),
     "kda_spec_verify": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,

@@ -263,7 +263,7 @@ size_t workspace_for(int B, int H, int dk, int dv, int n_seg) {
 kda_status_t prefill_entry(const void* q, const void* k, const void* v, const float* log_alpha, const void* gate,
                            bool gmode, const float* beta, const float* S0, void* o, float* S_T, int B, int T, int H, int dk,
                            int dv, int chunk, kda_dtype_t dt, int ckpt_every, float* S_ckpt, int seg_len,
-                           int n_vs, void* workspace, size_t workspace_bytes, void* stream);
+                           int n_vs, void* workspace, size_t workspace_bytes, void* stream, bool side_ok = true);
 
 }  // namespace
 
@@ -385,11 +385,12 @@ kda_status_t kda_chunk_prefill_gate(const void* q, const void* k, const void* v,
 namespace {
 
 // Every prefill entry point: the decay input is log_alpha (fp32) or, with gmode, gate (bf16 raw
-// gate pre-activation).
+// gate pre-activation).  side_ok = false keeps a sequence split entirely on `stream` (segment 0
+// then the transition/increment pass, one after the other; no stream or event of the library's).
 kda_status_t prefill_entry(const void* q, const void* k, const void* v, const float* log_alpha, const void* gate,
                            bool gmode, const float* beta, const float* S0, void* o, float* S_T, int B, int T, int H, int dk,
                            int dv, int chunk, kda_dtype_t dt, int ckpt_every, float* S_ckpt, int seg_len,
-                           int n_vs, void* workspace, size_t workspace_bytes, void* stream) {
+                           int n_vs, void* workspace, size_t workspace_bytes, void* stream, bool side_ok) {
     kda_status_t st = check_prefill_shape(B, T, H, dk, dv, chunk, dt);
     if (st != KDA_OK) return st;
     if (gmode && (dt != KDA_BF16 || !kda::prefill_dual_supported(dk, dv, chunk, false)))
@@ -557,7 +558,7 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
         // caller's earlier work, join before the scan.  One host thread at a time per library, so
         // the shared fork/join events are recorded and waited in order.
         std::lock_guard<std::mutex> lock(g_side_mu);
-        SideStream* side = ns > 2 ? side_stream() : nullptr;
+        SideStream* side = (ns > 2 && side_ok) ? side_stream() : nullptr;
         hipStream_t s0s = side ? side->stream : s;
         if (side) {
             if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
@@ -623,6 +624,18 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
 }
 
 }  // namespace
+
+namespace kda {
+
+kda_status_t prefill_on_stream(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                               const float* S0, void* o, float* S_T, int B, int T, int H, int dk, int dv, int chunk,
+                               kda_dtype_t dt, int seg_len, int n_vs, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return prefill_entry(q, k, v, log_alpha, nullptr, false, beta, S0, o, S_T, B, T, H, dk, dv, chunk, dt, 0, nullptr,
+                         seg_len, n_vs, workspace, workspace_bytes, stream, false);
+}
+
+}  // namespace kda
 
 extern "C" {
 

@@ -99,5 +99,11 @@ hipError_t launch_decode(int dk, bool f32, const DecodeArgs& a, hipStream_t stre
 // dst[i] = src ? src[i] : 0 for n floats
 hipError_t launch_state_copy(float* dst, const float* src, long long n, hipStream_t stream);
 
+// kda_chunk_prefill_ex with every launch of a sequence split on `stream` itself (no second stream
+// of the library, nothing created or allocated); the workspace is the caller's.
+kda_status_t prefill_on_stream(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                               const float* S0, void* o, float* S_T, int B, int T, int H, int dk, int dv, int chunk,
+                               kda_dtype_t dt, int seg_len, int n_vs, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 }  // namespace kda

@@ -25,7 +25,8 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
  *    never allocates, frees or retains them.  Scratch memory comes only from
- *    the caller's `workspace`.
+ *    the caller's `workspace` (kda_chunk_prefill_noalloc: from a fixed device
+ *    array inside the library).
  *  - Layouts are contiguous row-major.  Pointers must be 16-byte aligned
  *    (beta: 4-byte aligned).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
@@ -256,6 +257,39 @@ kda_status_t kda_spec_commit(const void *q, const void *k, const void *v,
                              const float *log_alpha, const float *beta, float *S,
                              const int *accepted, int N, int m, int H, int dk, int dv,
                              kda_dtype_t dtype, void *stream);
+
+/*
+ * Largest workspace kda_chunk_prefill_noalloc can serve: the bytes of the device
+ * array it uses in place of a caller workspace (one per GPU the library runs on,
+ * held until the process ends).  64 MiB covers, for example, a 1M-token sequence
+ * of 16 heads at d = 128 split into 17 segments (49 MiB).
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * kda_chunk_prefill_ex for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument, and no call to hipMalloc, hipFree or any
+ * other allocating routine.  A sequence split takes its transitions, increments
+ * and entry states from a fixed device array of KDA_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library, and every one of its launches runs on `stream` (segment 0
+ * and the transition/increment pass one after the other, not side by side).
+ *
+ *   arguments as for kda_chunk_prefill_ex, without workspace / workspace_bytes
+ *   returns KDA_ERR_WORKSPACE when kda_chunk_prefill_workspace_bytes_ex(..., seg_len)
+ *   exceeds KDA_NOALLOC_SCRATCH_BYTES (choose a longer seg_len, or call
+ *   kda_chunk_prefill_ex with a workspace); other errors as for kda_chunk_prefill_ex.
+ *
+ * All calls on one GPU share that GPU's array, and it keeps the last call's contents (every
+ * byte a call reads was written earlier by the same call).  Calls that overlap on one GPU —
+ * enqueued on different streams with no ordering between them, or from several host threads
+ * at once — race on it; callers serialise them.
+ */
+kda_status_t kda_chunk_prefill_noalloc(const void *q, const void *k, const void *v,
+                                       const float *log_alpha, const float *beta, const float *S0,
+                                       void *o, float *S_T,
+                                       int B, int T, int H, int dk, int dv, int chunk,
+                                       kda_dtype_t dtype, int seg_len, int n_vs, void *stream);
 
 #ifdef __cplusplus
 }

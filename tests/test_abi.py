@@ -337,3 +337,29 @@ def test_spec_long_block_never_needs_workspace(lib, host_only):
             st = _spec(lib, fn, N=1, m=m, H=1, dt=dt)
             assert st in (OK, DEVICE), (fn, m, dt, st)
 
+
+def _noalloc(lib, B=1, T=128, H=2, d=128, chunk=64, dt=BF16, seg=0, nvs=0, q=_ptrs(0), k=_ptrs(1),
+             v=_ptrs(2), la=_ptrs(3), beta=_ptrs(4), S0=None, o=_ptrs(5), S_T=None):
+    vp = ctypes.c_void_p
+    return lib.kda_chunk_prefill_noalloc(vp(q), vp(k), vp(v), vp(la), vp(beta), vp(S0), vp(o),
+                                         vp(S_T), B, T, H, d, d, chunk, dt, seg, nvs, None)
+
+
+def test_noalloc_validation(lib, host_only):
+    """The allocation-free prefill validates like kda_chunk_prefill_ex and refuses, before
+    anything is enqueued, a split whose scratch would exceed its fixed device array."""
+    assert _noalloc(lib, d=96) == UNSUPPORTED
+    assert _noalloc(lib, B=-1) == INVALID
+    assert _noalloc(lib, q=None) == INVALID
+    assert _noalloc(lib, o=_ptrs(0) + 64) == INVALID          # o over q
+    assert _noalloc(lib, seg=100) == INVALID                  # not a multiple of the chunk
+    assert _noalloc(lib, B=0, q=None, k=None, v=None, la=None, beta=None, o=None) == OK
+    # 56 heads x 1M tokens in 4096-token segments: about 11 GiB of scratch, over the limit
+    need = lib.kda_chunk_prefill_workspace_bytes_ex(1, 1 << 20, 56, 128, 128, 64, BF16, 4096)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, T=1 << 20, H=56, seg=4096) == WORKSPACE
+    # the 1M-token, 16-head workload fits, on its own 64K segments and on the automatic plan
+    assert lib.kda_chunk_prefill_workspace_bytes_ex(1, 1 << 20, 16, 128, 128, 64, BF16,
+                                                    1 << 16) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.kda_chunk_prefill_workspace_bytes(1, 1 << 20, 16, 128, 128, 64,
+                                                 BF16) <= _lib.NOALLOC_SCRATCH_BYTES
