@@ -62,6 +62,36 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(out_dir: str | None = None) -> str:
+    """libkda.so with its host code (argument validation, planning, launch set-up in
+    kda_api.cpp) built by g++ under AddressSanitizer and UndefinedBehaviorSanitizer, linked with
+    the device objects of the regular build (run build() first).  Load it with gcc's libasan and
+    libubsan preloaded; the device code is unchanged."""
+    out_dir = out_dir or os.path.join(BUILD_DIR, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    objs = sorted(os.path.join(BUILD_DIR, f) for f in os.listdir(BUILD_DIR) if f.endswith(".hip.o"))
+    if not objs:
+        raise RuntimeError("no device objects in _build: run build() first")
+    api_obj = os.path.join(out_dir, "kda_api.o")
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", *san, "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+           os.path.join(CSRC, "kda_api.cpp"), "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    lib = os.path.join(out_dir, "libkda.so")
+    cmd = ["g++", "-shared", *san, "-o", lib, api_obj, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if sys.argv[1:] == ["sanitized"]:
+        print(build_sanitized())
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -28,8 +28,15 @@ _LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+def build(force: bool = True, sanitized_out: str | None = None) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math).  With sanitized_out, build a copy
+    at that path under AddressSanitizer and UndefinedBehaviorSanitizer instead."""
+    if sanitized_out:
+        cmd = ["gcc", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+               "-Wall", "-Wextra", "-o", sanitized_out, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        return sanitized_out
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
