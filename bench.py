@@ -387,46 +387,65 @@ def cpu_baseline_long(gen, heads=1):
 
 
 def measure_peaks():
-    """Re-measured peaks on this GPU: a dense bf16 GEMM (8192^3 through torch.matmul), a read
-    stream (torch.sum over 4 GiB of fp32) and a device copy (2 GiB read + 2 GiB written)."""
+    """Re-measured peaks on this GPU: dense bf16 GEMMs through torch.matmul (8192^3 and 16384^3,
+    the faster reported), and HBM streams from the bandwidth probes of libkda_peaks.so (a 4 GiB
+    read stream, a 2 GiB + 2 GiB device copy and a 2 GiB in-place read-modify-write, 16-byte
+    non-temporal accesses), with torch's own device copy beside them."""
+    import ctypes
     import torch
+    from chunked_gated_delta_13_amd import build as kbuild
     res = {}
-    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
-    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
-    for _ in range(3):
-        c = a @ b
-    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(20):
-        c = a @ b
-    ev1.record()
-    torch.cuda.synchronize()
-    res["bf16_gemm_TFLOPs"] = 2 * 8192 ** 3 * 20 / (ev0.elapsed_time(ev1) / 1e3) / 1e12
-    del a, b, c
-    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        r = x.sum()
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(10):
-        r = x.sum()
-    ev1.record()
-    torch.cuda.synchronize()
-    res["hbm_read_GBps"] = x.numel() * 4 * 10 / (ev0.elapsed_time(ev1) / 1e3) / 1e9
-    del r
-    y = torch.empty(1 << 29, dtype=torch.float32, device="cuda")
-    src = x[: 1 << 29]
-    for _ in range(3):
-        y.copy_(src)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(10):
-        y.copy_(src)
-    ev1.record()
-    torch.cuda.synchronize()
-    res["hbm_copy_GBps"] = 2 * y.numel() * 4 * 10 / (ev0.elapsed_time(ev1) / 1e3) / 1e9
-    del x, y, src
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(reps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3 / reps
+
+    best = 0.0
+    for n in (8192, 16384):
+        a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        t = timed(lambda: a @ b, 10)
+        best = max(best, 2 * n ** 3 / t / 1e12)
+        del a, b
+    res["bf16_gemm_TFLOPs"] = best
+    lib = ctypes.CDLL(kbuild.PEAKS_LIB)
+    lib.kda_peak_read_sink_floats.restype = ctypes.c_size_t
+    lib.kda_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kda_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")           # 4 GiB
+    sink = torch.empty(lib.kda_peak_read_sink_floats(), dtype=torch.float32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    nb = x.numel() * 4
+
+    def rd():
+        assert lib.kda_peak_read(ctypes.c_void_p(x.data_ptr()), nb, ctypes.c_void_p(sink.data_ptr()), sp) == 0
+
+    res["hbm_read_GBps"] = nb / timed(rd, 10) / 1e9
+    half = 1 << 29                                                       # 2 GiB of floats
+    src, dst = x[:half], x[half:]
+
+    def cp():
+        assert lib.kda_peak_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                 half * 4, sp) == 0
+
+    res["hbm_copy_GBps"] = 2 * half * 4 / timed(cp, 10) / 1e9
+    lib.kda_peak_rmw.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+
+    def rmw():
+        assert lib.kda_peak_rmw(ctypes.c_void_p(src.data_ptr()), half * 4, 1.0, 0.0, sp) == 0
+
+    res["hbm_rmw_GBps"] = 2 * half * 4 / timed(rmw, 10) / 1e9
+    res["torch_copy_GBps"] = 2 * half * 4 / timed(lambda: dst.copy_(src), 10) / 1e9
+    del x, sink, src, dst
     torch.cuda.empty_cache()
     log(f"[peaks] {res}")
     return res
@@ -559,12 +578,11 @@ def main():
     if not args.prefill_only:
         peaks = measure_peaks()
         rf = result["roofline"]
-        rf["peak_measured"] = {"hbm_read_GBps": peaks["hbm_read_GBps"], "hbm_copy_GBps": peaks["hbm_copy_GBps"],
-                               "bf16_gemm_TFLOPs": peaks["bf16_gemm_TFLOPs"]}
+        rf["peak_measured"] = dict(peaks)
         rf["frac_of_measured_read"] = rf["achieved"] / peaks["hbm_read_GBps"]
         rf["useful_frac_of_measured_gemm"] = rf["useful_tflops"] / peaks["bf16_gemm_TFLOPs"]
         if "decode" in result:
-            result["decode"]["frac_of_measured_copy"] = result["decode"]["state_GBps"] / peaks["hbm_copy_GBps"]
+            result["decode"]["frac_of_measured_rmw"] = result["decode"]["state_GBps"] / peaks["hbm_rmw_GBps"]
     print(json.dumps(result), flush=True)
 
 

@@ -17,6 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
+PEAKS_LIB = os.path.join(HERE, "libkda_peaks.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
@@ -45,20 +46,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
-                  if f.endswith(".hip") or f.endswith(".cpp"))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """libkda.so from csrc/*.hip and csrc/*.cpp, and the benchmark's bandwidth probes
+    (libkda_peaks.so, from csrc/bench/) beside it."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") or f.endswith(".cpp"))
+    probe_srcs = sorted(os.path.join(CSRC, "bench", f) for f in os.listdir(os.path.join(CSRC, "bench"))
+                        if f.endswith(".hip"))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+        probe_objs = list(ex.map(_compile, probe_srcs))
+    _link(objs, LIB)
+    _link(probe_objs, PEAKS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 
@@ -69,7 +80,9 @@ def build_sanitized(out_dir: str | None = None) -> str:
     libubsan preloaded; the device code is unchanged."""
     out_dir = out_dir or os.path.join(BUILD_DIR, "asan")
     os.makedirs(out_dir, exist_ok=True)
-    objs = sorted(os.path.join(BUILD_DIR, f) for f in os.listdir(BUILD_DIR) if f.endswith(".hip.o"))
+    probes = {os.path.basename(f) + ".o" for f in os.listdir(os.path.join(CSRC, "bench"))}
+    objs = sorted(os.path.join(BUILD_DIR, f) for f in os.listdir(BUILD_DIR)
+                  if f.endswith(".hip.o") and f not in probes)
     if not objs:
         raise RuntimeError("no device objects in _build: run build() first")
     api_obj = os.path.join(out_dir, "kda_api.o")

@@ -429,8 +429,10 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float l2 = okt[i] ? fminf(fmaxf(l4[u], kLogAlphaMin), 0.0f) * kLog2e : 0.0f;
-                    run[u] = (i % G == 0) ? l2 : run[u] + l2;
+                    // clamp to [-5, 0] (rows past the end add nothing), then accumulate the
+                    // log2-decay in one rounding per token
+                    const float l = okt[i] ? __builtin_amdgcn_fmed3f(l4[u], kLogAlphaMin, 0.0f) : 0.0f;
+                    run[u] = (i % G == 0) ? l * kLog2e : fmaf(l, kLog2e, run[u]);
                     g[i][u] = run[u];
                 }
                 if (i % G == G - 1)

@@ -257,8 +257,8 @@ __device__ __forceinline__ void pipe_chunk_waves(const PrefillArgs& a, const Pip
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float l2 = okt[i] ? fminf(fmaxf(l4[e], kLogAlphaMin), 0.0f) * kLog2e : 0.0f;
-                run[e] = (i % G == 0) ? l2 : run[e] + l2;
+                const float l = okt[i] ? __builtin_amdgcn_fmed3f(l4[e], kLogAlphaMin, 0.0f) : 0.0f;
+                run[e] = (i % G == 0) ? l * kLog2e : fmaf(l, kLog2e, run[e]);
                 g[i][e] = run[e];
             }
             if (i % G == G - 1)
@@ -726,22 +726,38 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
         barrier_lds();
 
         // ---- interval 3: S <- Diag(2^{g_C}) S + K'^T U ----
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const f32x4_t gm = *reinterpret_cast<const KDA_LDS f32x4_t*>(pGs + 16 * it);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) st[it][ct][j] *= gm[j];
-#pragma unroll
-            for (int kb = 0; kb < NTB; ++kb) {
-                Frag<OpT> fkp;
+        // 16 steps (row tile it, contraction block kb); the K'^T fragment of step i is requested
+        // ULA steps ahead and the decay row of tile it one tile ahead, so that their LDS latency
+        // overlaps the products of the steps between
+        {
+            constexpr int NUS = NIT * NTB, ULA = 4;
+            Frag<OpT> fkb[ULA + 1];
+            f32x4_t gmv[2];
+            auto u_load = [&](auto Ic) {
+                constexpr int i = decltype(Ic)::value;
+                constexpr int it = i / NTB, kb = i % NTB;
+                constexpr int hi = (8 * it) & 48;
                 const KDA_LDS OpT* const kb0 = ((it & 1) ? pKs1 : pKs0) + 16 * it * PT;
-                const int hi = (8 * it) & 48;
-                frag_ld2(fkp, kb0 + ((32 * kb) ^ hi), kb0 + ((32 * kb + 16) ^ hi));
+                frag_ld2(fkb[i % (ULA + 1)], kb0 + ((32 * kb) ^ hi), kb0 + ((32 * kb + 16) ^ hi));
+            };
+            gmv[0] = *reinterpret_cast<const KDA_LDS f32x4_t*>(pGs);
+            static_for<0, ULA>([&](auto Ic) { u_load(Ic); });
+            static_for<0, NUS>([&](auto Ic) {
+                constexpr int i = decltype(Ic)::value;
+                constexpr int it = i / NTB, kb = i % NTB;
+                if constexpr (i + ULA < NUS) u_load(std::integral_constant<int, i + ULA>{});
+                if constexpr (kb == 0 && it + 1 < NIT)
+                    gmv[(it + 1) & 1] = *reinterpret_cast<const KDA_LDS f32x4_t*>(pGs + 16 * (it + 1));
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (kb == 0) {
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) st[it][ct] = mma(fkp, fU[kb][ct], st[it][ct]);
-            }
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) st[it][ct][j] *= gmv[it & 1][j];
+                }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) st[it][ct] = mma(fkb[i % (ULA + 1)], fU[kb][ct], st[it][ct]);
+            });
         }
         if (a.s_ckpt) {   // the state after a full chunk ending on a multiple of ckpt_every
             const long long pend = c0 + C;
