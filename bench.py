@@ -166,7 +166,7 @@ def bench_prefill_gate(kda, gen, w, d, steps, warmup):
 
 def bench_long(kda, gen, steps, warmup):
     """The 1M-token prefill with the workload's 64K-token segments, then with the library's own
-    plan (segment 0 longer, run beside the transition/increment pass of the middle segments)."""
+    plan (equal segments, few enough that all run at once on fewer workgroups than compute units)."""
     import torch
     w = gen.WORKLOADS["long_1m"]
     log(f"[long] generating {w.note} on the device")
@@ -567,12 +567,17 @@ def main():
         wl, lres = bench_long(kda, gen, nsteps, 1)
         (lwall, _), (awall, _) = lres
         auto_seg, _ = kda.prefill_plan(wl.B, wl.T, wl.H, wl.dk, wl.dv, wl.chunk)
+        # algorithmic bytes of one pass over the sequence: what any split must move at least
+        one_pass = wl.B * wl.T * wl.H * BYTES_PER_TOKEN_HEAD + 2 * wl.B * wl.H * wl.dk * wl.dv * 4
         result["long_context"] = {"workload": wl.note, "seg_len": wl.segment, "steps": nsteps,
                                   "ms_per_step": lwall / nsteps * 1e3,
                                   "tokens_per_s": wl.B * wl.T * nsteps / lwall,
-                                  "automatic_plan": {"seg_len_after_first": auto_seg,
+                                  "alg_bytes_one_pass": one_pass,
+                                  "frac_of_hbm_peak": one_pass * nsteps / lwall / (HBM_PEAK_GBS * 1e9),
+                                  "automatic_plan": {"seg_len": auto_seg,
                                                      "ms_per_step": awall / nsteps * 1e3,
-                                                     "tokens_per_s": wl.B * wl.T * nsteps / awall}}
+                                                     "tokens_per_s": wl.B * wl.T * nsteps / awall,
+                                                     "frac_of_hbm_peak": one_pass * nsteps / awall / (HBM_PEAK_GBS * 1e9)}}
         if not args.no_cpu_baseline:
             result["long_context"]["cpu_baseline"] = cpu_baseline_long(gen)
     if not args.prefill_only:

@@ -173,12 +173,6 @@ int spec_chunk(int m, kda_dtype_t dt) {
     return 64;
 }
 
-// Per-chunk cost of the transition/increment work relative to an output pass at the same shape,
-// measured on the MI355X at d = 128: the shared pass of 8-wave shapes 6.9 us against 5.2 us per
-// 64-token chunk; 4-wave shapes run two separate passes.
-constexpr double kSharedPassCost = 1.3;
-constexpr double kTwoPassCost = 2.0;
-
 // Segments of a split: segment 0 holds seg_len + shift tokens, every later one seg_len (the last
 // one possibly fewer).
 long long segment_count(long long T, long long seg_len, long long shift) {
@@ -187,12 +181,11 @@ long long segment_count(long long T, long long seg_len, long long shift) {
 }
 
 // The automatic plan: column slices first (no extra work beyond the shared per-chunk tiles),
-// then segments when even that leaves most compute units idle.  A split runs in two phases of
-// units * (n - 1) workgroups each, one per compute unit: first segment 0 from S0 with its outputs
-// beside the transitions and increments of segments 1 .. n-2, then segments 1 .. n-1 from their
-// entry states.  A phase never takes every compute unit (on the MI355X, phases that needed all
-// 256 at once ran up to 13% slower at times).  Segment 0 is longer than the others by the cost
-// ratio of the two kinds of pass, so that both halves of the first phase end together.
+// then segments when even that leaves most compute units idle.  The widest step of a split runs
+// every segment at once (segment 0 from S0 beside the zero-start runs of the others), one
+// workgroup per unit and segment, and it never takes every compute unit (on the MI355X, launches
+// that needed all 256 at once ran up to 13% slower at times).  Segments are of equal length (the
+// last one possibly shorter): every step runs the same work on each of them.
 void auto_plan(int B, int T, int H, int dk, int dv, int chunk, bool f32, int* seg_len, int* n_vs,
                long long* shift) {
     const long long cus = cu_count();
@@ -203,26 +196,22 @@ void auto_plan(int B, int T, int H, int dk, int dv, int chunk, bool f32, int* se
     // intra-chunk work; the sequence split below is what shortens the chain of chunks.
     const bool eight = kda::prefill_waves(dk, dv, f32) == 8;
     int vs = (dv == 128 && !eight && 2 * bh <= cus) ? 2 : 1;
-    long long seg = T, sh = 0;
+    long long seg = T;
     const long long units = bh * vs;
     const long long lmin = min_segment(T);
     if (units > 0 && 2 * units <= cus && (long long)T >= 3 * lmin) {
-        long long m = (cus - 1) / units;   // segments after the first
-        if (m > T / lmin - 1) m = T / lmin - 1;
-        if (m >= 2) {
-            const double r = kda::prefill_dual_supported(dk, dv / vs, chunk, f32) ? kSharedPassCost : kTwoPassCost;
-            // L: the nearest multiple of the chunk; segment 0 takes what the others leave (if
-            // anything: else all segments have L tokens but the last)
-            long long L = ((long long)((double)T / (r + (double)m)) + chunk / 2) / chunk * chunk;
-            if (L < chunk) L = chunk;
-            const long long rest = (long long)T - (m + 1) * L;
-            sh = rest > 0 ? (rest + chunk - 1) / chunk * chunk : 0;
+        long long n = (cus - 1) / units;   // segments
+        if (n > T / lmin) n = T / lmin;
+        if (n >= 3) {
+            // whole chunks, rounded up so that n segments cover the sequence
+            long long L = ((long long)T + n - 1) / n;
+            L = (L + chunk - 1) / chunk * chunk;
             seg = L;
         }
     }
     if (seg_len) *seg_len = (int)(seg > 0 ? seg : chunk);
     if (n_vs) *n_vs = vs;
-    if (shift) *shift = seg > 0 && seg < T ? sh : 0;
+    if (shift) *shift = 0;
 }
 
 // Resolve an explicit or automatic plan.  n_seg == 1 means no split.  An explicit seg_len gives
@@ -253,11 +242,25 @@ kda_status_t resolve_plan(int B, int T, int H, int dk, int dv, int chunk, kda_dt
     return KDA_OK;
 }
 
+// Split workspace: transitions M [B*H, n_seg-1, dk, dk] (slot s for segment s; slot 0 unused),
+// increments H [B*H, n_seg-1, dk, dv] (likewise), entry states S_in [B*H, n_seg, dk, dv] (slot s
+// for segment s >= 1; slot 0 holds the last segment's increment), then the transition pass's
+// chunk counts [B*H, n_seg-1, 2] int32 (room for two column slices), padded to 16 bytes.
 size_t workspace_for(int B, int H, int dk, int dv, int n_seg) {
     if (n_seg <= 1) return 0;
     const size_t bh = (size_t)B * H;
     const size_t mats = (size_t)(n_seg - 1) * ((size_t)dk * dk + (size_t)dk * dv) + (size_t)n_seg * dk * dv;
-    return bh * mats * sizeof(float);
+    const size_t counts = (bh * (size_t)(n_seg - 1) * 2 * sizeof(int) + 15) / 16 * 16;
+    return bh * mats * sizeof(float) + counts;
+}
+
+// A launch description with every optional part off.
+PrefillArgs blank_prefill_args() {
+    PrefillArgs a;
+    memset(&a, 0, sizeof(a));
+    a.out_seg = -1;
+    a.tail_seg = -1;
+    return a;
 }
 
 kda_status_t prefill_entry(const void* q, const void* k, const void* v, const float* log_alpha, const void* gate,
@@ -468,8 +471,7 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     const bool f32 = dt == KDA_F32;
     const long long SS = (long long)dk * dv;
 
-    PrefillArgs a;
-    memset(&a, 0, sizeof(a));
+    PrefillArgs a = blank_prefill_args();
     a.q = q;
     a.k = k;
     a.v = v;
@@ -506,91 +508,120 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     }
 
     // ---- sequence split ----
-    // Phase 1: segment 0 runs from S0 with its outputs (on a side stream) while the transitions
-    // M_s and increments H_s of segments 1 .. ns-2 are formed (on the caller's stream); segment 0's
-    // final state is the entry state S_in(1).  Then the scan S_in(s+1) = M_s S_in(s) + H_s for
-    // s = 1 .. ns-2, and phase 2 runs segments 1 .. ns-1 from their entry states with outputs.
+    // Segment s >= 1 depends on its entry state only through the transition M_s, and the entry
+    // state's influence dies out along the segment: for unit keys and beta in [0, 2] every token's
+    // transition (I - beta k k^T) Diag(alpha) is a contraction, and the decay shrinks it further.
+    //  1. A transition pass over segments 1 .. ns-1 (identity start, zero values; for 8-wave shapes
+    //     together with the increment H_s) stops once every entry of its transition has fallen below
+    //     2^-126, stores the transition as zeros and records how many chunks it ran; a transition
+    //     that never dies is formed over the whole segment (count -1).
+    //  2. Segments 1 .. ns-1 run with outputs from a zero start (in the shared 8-wave pass, only
+    //     those whose transition died: the others have their increment already); their final states
+    //     are the increments H_s.  Segment 0 runs from S0 with its outputs, on a side stream beside
+    //     steps 1-2, or inside step 2's launch; its final state is the entry state S_in(1).
+    //  3. The scan S_in(s+1) = M_s S_in(s) + H_s, s = 1 .. ns-2.
+    //  4. Each segment s >= 1 reruns from S_in(s) the chunks its transition pass counted (all of
+    //     them for count -1), overwriting those outputs.
+    // Past that count the entry state adds less than d_k 2^-126 times its own size to the state,
+    // so the zero-start outputs stand (exact up to rounding); where the transition never dies, the
+    // steps are the plain two-pass split.  Sources: "Kimi K3's architecture" (orkas.ai), "The bill
+    // comes due in the serving stack" (transition and zero-start state combine across segments);
+    // "Inside Kimi K3" (academa.ai lecture), sequence paragraph (the diagonal gate scales down
+    // what the state keeps from earlier tokens).
     float* ws = reinterpret_cast<float*>(workspace);
     const long long bh = (long long)B * H;
     float* wsM = ws;
     float* wsH = wsM + bh * (ns - 1) * SS;
     float* wsSin = wsH + bh * (ns - 1) * SS;
+    int* wsZ = reinterpret_cast<int*>(wsSin + bh * ns * SS);
     a.seg_shift = shift;
+    a.n_seg_total = ns;
+    const bool dual = kda::prefill_dual_supported(dk, dvw, chunk, f32);
 
-    PrefillArgs p0 = a;  // segment 0 from S0, with outputs and checkpoints; final state -> S_in(1)
-    p0.o = o;
-    p0.s_in = S0;
-    p0.sin_bh_stride = SS;
-    p0.sin_seg_stride = 0;
-    p0.init_mode = S0 ? 1 : 0;
-    p0.s_out = wsSin + SS;
-    p0.sout_bh_stride = (long long)ns * SS;
-    p0.sout_seg_stride = 0;
-    p0.out_seg = 0;
-    p0.seg0 = 0;
-    p0.n_seg_launch = 1;
-    p0.n_units = (int)bh;
-    p0.zero_values = 0;
-    if (n_ckpt > 0) {   // the passes that run from true entry states write the checkpoints
-        p0.s_ckpt = S_ckpt;
-        p0.ckpt_every = ckpt_every;
-        p0.n_ckpt = n_ckpt;
+    PrefillArgs pt = a;  // step 1: transitions of segments 1 .. ns-1, early stop
+    pt.o = nullptr;
+    pt.s_in = nullptr;
+    pt.init_mode = 2;
+    pt.zero_values = 1;
+    pt.s_out = wsM;
+    pt.sout_bh_stride = (long long)(ns - 1) * SS;
+    pt.sout_seg_stride = SS;
+    pt.out_seg = -1;
+    pt.seg0 = 1;
+    pt.n_seg_launch = ns - 1;
+    pt.n_units = (int)(bh * (ns - 1));
+    pt.probe = 1;
+    pt.z_out = wsZ;
+    pt.tail_seg = ns - 1;   // the last segment's transition and increment are not kept
+    pt.s_tail = nullptr;
+    if (dual) {   // with the increment: the decay and intra-chunk work is shared
+        pt.init_mode = 0;
+        pt.zero_values = 0;
+        pt.s_out = wsH;
+        pt.s_aux = wsM;
+        pt.saux_bh_stride = (long long)(ns - 1) * SS;
+        pt.saux_seg_stride = SS;
     }
 
-    PrefillArgs pm = a;  // M_s: identity columns, zero values, no output (segments 1 .. ns-2)
-    pm.o = nullptr;
-    pm.s_in = nullptr;
-    pm.init_mode = 2;
-    pm.zero_values = 1;
-    pm.s_out = wsM;
-    pm.sout_bh_stride = (long long)(ns - 1) * SS;
-    pm.sout_seg_stride = SS;
-    pm.out_seg = -1;
-    pm.seg0 = 1;
-    pm.n_seg_launch = ns - 2;
-    pm.n_units = (int)(bh * (ns - 2));
-    // The shared transition/increment pass runs the caller's chunk (at 64 tokens the two states
-    // spill a few registers outside the chunk loop, and the pass is still faster than at 32).
-    const int dchunk = chunk;
+    PrefillArgs pz = a;  // step 2: segments from a zero start with outputs; increments H_s
+    pz.o = o;
+    pz.s_in = S0;
+    pz.sin_bh_stride = SS;
+    pz.sin_seg_stride = 0;
+    pz.init_mode = 0;
+    pz.s_out = wsH;
+    pz.sout_bh_stride = (long long)(ns - 1) * SS;
+    pz.sout_seg_stride = SS;
+    pz.out_seg = -1;
+    pz.seg0 = 1;
+    pz.n_seg_launch = ns - 1;
+    pz.n_units = (int)(bh * (ns - 1));
+    pz.z_in = wsZ;
+    pz.z_gate = dual ? 1 : 0;
+    pz.tail_seg = ns - 1;   // the last segment's increment goes to S_in slot 0
+    pz.s_tail = wsSin;
+    pz.stail_bh_stride = (long long)ns * SS;
+    pz.s_head = wsSin + SS;   // segment 0's final state is S_in(1)
+    pz.shead_bh_stride = (long long)ns * SS;
+    if (n_ckpt > 0) {
+        pz.s_ckpt = S_ckpt;
+        pz.ckpt_every = ckpt_every;
+        pz.n_ckpt = n_ckpt;
+    }
 
     {
-        // segment 0 overlaps the transition/increment pass on a side stream: fork after the
+        // With a side stream, segment 0 (its own launch) overlaps steps 1-2: fork after the
         // caller's earlier work, join before the scan.  One host thread at a time per library, so
         // the shared fork/join events are recorded and waited in order.
         std::lock_guard<std::mutex> lock(g_side_mu);
-        SideStream* side = (ns > 2 && side_ok) ? side_stream() : nullptr;
-        hipStream_t s0s = side ? side->stream : s;
+        SideStream* side = side_ok ? side_stream() : nullptr;
         if (side) {
             if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
                 return KDA_ERR_DEVICE;
+            PrefillArgs p0 = pz;  // segment 0 alone, from S0
+            p0.init_mode = S0 ? 1 : 0;
+            p0.seg0 = 0;
+            p0.n_seg_launch = 1;
+            p0.n_units = (int)bh;
+            p0.z_gate = 0;
+            if (kda::launch_prefill(dk, dvw, chunk, f32, p0, side->stream) != hipSuccess) return KDA_ERR_DEVICE;
+        } else {      // segment 0 joins step 2's launch
+            pz.init_mode = S0 ? 3 : 0;
+            pz.seg0 = 0;
+            pz.n_seg_launch = ns;
+            pz.n_units = (int)(bh * ns);
         }
-        if (kda::launch_prefill(dk, dvw, chunk, f32, p0, s0s) != hipSuccess) return KDA_ERR_DEVICE;
-        if (ns > 2) {
-            if (kda::prefill_dual_supported(dk, dvw, dchunk, f32)) {
-                PrefillArgs pd = pm;  // M_s and H_s together: the decay and intra-chunk work is shared
-                pd.init_mode = 0;
-                pd.zero_values = 0;
-                pd.s_out = wsH;
-                pd.s_aux = wsM;
-                pd.saux_bh_stride = pm.sout_bh_stride;
-                pd.saux_seg_stride = pm.sout_seg_stride;
-                if (kda::launch_prefill_dual(dk, dvw, dchunk, f32, pd, s) != hipSuccess) return KDA_ERR_DEVICE;
-            } else {
-                if (kda::launch_prefill(dk, dvw, chunk, f32, pm, s) != hipSuccess) return KDA_ERR_DEVICE;
-                PrefillArgs ph = pm;  // H_s: zero start, real values, no output
-                ph.init_mode = 0;
-                ph.zero_values = 0;
-                ph.s_out = wsH;
-                if (kda::launch_prefill(dk, dvw, chunk, f32, ph, s) != hipSuccess) return KDA_ERR_DEVICE;
-            }
-        }
+        const hipError_t e1 = dual ? kda::launch_prefill_dual(dk, dvw, chunk, f32, pt, s)
+                                   : kda::launch_prefill(dk, dvw, chunk, f32, pt, s);
+        if (e1 != hipSuccess) return KDA_ERR_DEVICE;
+        if (kda::launch_prefill(dk, dvw, chunk, f32, pz, s) != hipSuccess) return KDA_ERR_DEVICE;
         if (side) {
             if (hipEventRecord(side->join, side->stream) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
                 return KDA_ERR_DEVICE;
         }
     }
 
-    kda::ScanArgs sa;
+    kda::ScanArgs sa;   // step 3
     sa.M = wsM;
     sa.Hinc = wsH;
     sa.S0 = S0;
@@ -598,9 +629,11 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     sa.BH = (int)bh;
     sa.n_seg = ns;
     sa.s_first = 1;   // S_in(1) was written by segment 0's pass
+    sa.z = wsZ;
+    sa.n_vs = vs;
     if (ns > 2 && kda::launch_scan(dk, sa, s) != hipSuccess) return KDA_ERR_DEVICE;
 
-    PrefillArgs pf = a;  // segments 1 .. ns-1 from their entry states, with outputs
+    PrefillArgs pf = a;  // step 4: segments 1 .. ns-1 from their entry states, as far as counted
     pf.o = o;
     pf.s_in = wsSin;
     pf.sin_bh_stride = (long long)ns * SS;
@@ -614,6 +647,11 @@ kda_status_t prefill_entry(const void* q, const void* k, const void* v, const fl
     pf.seg0 = 1;
     pf.n_seg_launch = ns - 1;
     pf.n_units = (int)(bh * (ns - 1));
+    pf.z_in = wsZ;
+    pf.z_limit = 1;
+    pf.tail_seg = ns - 1;   // cut short: S_T is the last segment's increment
+    pf.s_tail = wsSin;
+    pf.stail_bh_stride = (long long)ns * SS;
     if (n_ckpt > 0) {
         pf.s_ckpt = S_ckpt;
         pf.ckpt_every = ckpt_every;
@@ -737,8 +775,7 @@ kda_status_t kda_spec_commit(const void* q, const void* k, const void* v, const 
 
     (void)hipGetLastError();
     const long long SS = (long long)dk * dv;
-    PrefillArgs a;
-    memset(&a, 0, sizeof(a));
+    PrefillArgs a = blank_prefill_args();
     a.q = q;
     a.k = k;
     a.v = v;

@@ -232,4 +232,18 @@ __device__ __forceinline__ void barrier_all() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Chunk count of the sequence split's unit (bh, segment s >= 1) from the counts of a transition
+// pass laid out [bh][n_seg_total - 1][n_vs]: the largest over the unit's column slices, -1 if any
+// slice's transition never fell below 2^-126.
+__device__ __forceinline__ int split_count(const int* z, int n_seg_total, int n_vs, int bh, int s) {
+    const int* p = z + ((long long)bh * (n_seg_total - 1) + (s - 1)) * n_vs;
+    int m = 0;
+    for (int v = 0; v < n_vs; ++v) {
+        const int c = p[v];
+        if (c < 0) return -1;
+        m = c > m ? c : m;
+    }
+    return m;
+}
+
 }  // namespace kda

@@ -21,7 +21,8 @@ struct PrefillArgs {
     const float* s_in;
     long long sin_bh_stride;
     long long sin_seg_stride;
-    int init_mode;            // 0: zeros, 1: load from s_in, 2: identity columns
+    int init_mode;            // 0: zeros, 1: load from s_in, 2: identity columns, 3: segment 0
+                              // loads s_in (its entry state), later segments start at zero
 
     // final state of a unit, written when out_seg < 0 or s == out_seg
     float* s_out;
@@ -54,6 +55,26 @@ struct PrefillArgs {
     float* s_ckpt;
     int ckpt_every;
     int n_ckpt;
+
+    // ---- short cut of the sequence split: an entry state's influence dies out ----
+    // Chunk counts per (b, h, segment s >= 1, column slice) at
+    //   z[((bh * (n_seg_total - 1)) + s - 1) * n_vs + vs]:
+    // the chunks a transition pass ran before every entry of its transition columns fell below
+    // 2^-126 (it then stops and stores the transition as zeros), or -1 if they never did.
+    int probe;                // 1: this transition pass stops early and writes z_out
+    int* z_out;
+    const int* z_in;          // counts of an earlier probe, read by the gate and the limit
+    int z_gate;               // 1: skip a unit s >= 1 whose count is -1 (the probe formed its increment)
+    int z_limit;              // 1: a unit s >= 1 runs only its count of chunks (all of them when -1)
+    int n_seg_total;          // segments per (b, h) of the whole split
+    // final state of the last segment (tail_seg): written to s_tail instead of s_out, or, with
+    // z_limit, copied from s_tail to s_out when the unit was cut short
+    float* s_tail;
+    long long stail_bh_stride;
+    int tail_seg;             // -1: none
+    // final state of segment 0, when set: written to s_head instead of s_out
+    float* s_head;
+    long long shead_bh_stride;
 };
 
 struct ScanArgs {
@@ -64,6 +85,10 @@ struct ScanArgs {
     int BH;
     int n_seg;
     int s_first;              // 0: start from S0; 1: start from S_in(1), already in place
+    // the transition pass's chunk counts (layout as in PrefillArgs, n_seg segments) or nullptr:
+    // a step whose transition died (count >= 0, stored as zeros) is S_in(s+1) = H_s, no product
+    const int* z;
+    int n_vs;
 };
 
 // Decode step (m = 1) or a block of m <= kDecodeMaxTokens tokens per (sequence, head) run from

@@ -96,7 +96,8 @@ struct PrefillCfg {
     static constexpr size_t oBeta = oD + al(4 * (NT == 4 ? NT + 3 : NT) * DK);   // D rows (+ products)
     static constexpr size_t oTot = oBeta + al(4 * C);
     static constexpr size_t oO = oTot + al(4 * 16 * DK);
-    static constexpr size_t LDS = oO + al(sizeof(TIn) * NW * 16 * PW);
+    static constexpr size_t oFlag = oO + al(sizeof(TIn) * NW * 16 * PW);   // early-stop flags [2][NW]
+    static constexpr size_t LDS = oFlag + al(4 * 2 * NW);
     static_assert(LDS <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 
@@ -161,7 +162,10 @@ template <> struct Quad<float> {
 // is shared and no output rows are formed.
 // GATE: the decay input is the raw gate pre-activation x (bf16) and log alpha = -5 sigmoid(x) is
 // formed on load, in place of an fp32 log alpha.
-template <class Cfg, bool DUAL, bool GATE>
+// PROBE: a transition pass that stops once its transition columns have died (every entry below
+// 2^-126), stores the transition as zeros and records the chunks it ran (the sequence split's
+// short cut); the dual pass always runs this way.
+template <class Cfg, bool DUAL, bool GATE, bool PROBE>
 __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs a) {
     using TIn = typename Cfg::TIn;
     using OpT = typename Cfg::OpT;
@@ -191,6 +195,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     KDA_LDS float* sBeta = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oBeta);
     KDA_LDS float* sTot = reinterpret_cast<KDA_LDS float*>(smem + Cfg::oTot);
     KDA_LDS TIn* sO = reinterpret_cast<KDA_LDS TIn*>(smem + Cfg::oO);
+    KDA_LDS int* sFlag = reinterpret_cast<KDA_LDS int*>(smem + Cfg::oFlag);
 
     // ---- unit of this workgroup; sibling column slices share an XCD (blockIdx % 8) ----
     const int bid = blockIdx.x;
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
                     st[it][NCT + ct][j] = (16 * it + 4 * lg + j == col) ? 1.0f : 0.0f;
                 }
             }
-    } else if (a.init_mode == 1) {
+    } else if (a.init_mode == 1 || (a.init_mode == 3 && s == 0)) {
         const float* sin = a.s_in + (long long)bh * a.sin_bh_stride + (long long)s * a.sin_seg_stride;
 #pragma unroll
         for (int it = 0; it < NIT; ++it)
@@ -382,15 +387,36 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     };
 
     const long long ntok = t_end - t_begin;
-    const int nchunks = ntok > 0 ? (int)((ntok + C - 1) / C) : 0;
+    int nchunks = ntok > 0 ? (int)((ntok + C - 1) / C) : 0;
+    // sequence split: skip a unit whose increment the transition pass already formed, or run only
+    // the chunks over which the entry state still matters (unit-uniform, before any barrier)
+    bool cut = false;
+    if (s > 0 && (a.z_gate || a.z_limit)) {
+        const int z = split_count(a.z_in, a.n_seg_total, a.n_vs, bh, s);
+        if (a.z_gate && z < 0) return;
+        if (a.z_limit && z >= 0 && z < nchunks) {
+            nchunks = z;
+            cut = true;
+        }
+    }
     if (nchunks > 0) {
         load_qk(t_begin);
         load_vb(t_begin);
     }
+    int died_at = -1;   // transition pass with early stop: chunks run before the transition died
 
     for (int c = 0; c < nchunks; ++c) {
         const long long c0 = t_begin + (long long)c * C;
         barrier_all();  // every wave's log-decay block has landed; the previous chunk's LDS reads are done
+        if (PROBE && c > 0) {   // every wave reads the same flags: a workgroup-uniform decision
+            bool alive = false;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) alive |= sFlag[((c - 1) & 1) * NW + w] != 0;
+            if (!alive) {
+                died_at = c;
+                break;
+            }
+        }
 
         // ================= A: commit prefetched values, per-segment cumulative decay =================
 #pragma unroll
@@ -789,6 +815,22 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
             }
         }
 
+        // early stop: does any transition entry of this wave still hold a normal float (exponent
+        // field not zero)?  Read at the top of the next chunk, after its barrier; the buffers
+        // alternate by chunk parity, so a flag is not overwritten before every wave has read it.
+        if constexpr (PROBE) {
+            constexpr int T0 = DUAL ? NCT : 0;
+            uint32_t ex = 0;
+#pragma unroll
+            for (int it = 0; it < NIT; ++it)
+#pragma unroll
+                for (int ct = T0; ct < T0 + NCT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ex |= __float_as_uint(st[it][ct][j]) & 0x7f800000u;
+            const bool wave_alive = __ballot(ex != 0) != 0;
+            if (lane == 0) sFlag[(c & 1) * NW + wave] = wave_alive ? 1 : 0;
+        }
+
         // checkpoint: the state after a multiple of ckpt_every tokens (full chunks only)
         if constexpr (!DUAL) {
             if (a.s_ckpt) {
@@ -810,37 +852,88 @@ __global__ __launch_bounds__(Cfg::NTH) void kda_prefill_kernel(const PrefillArgs
     }
 
     // ---- final state ----
-    if constexpr (DUAL) {
-        float* sx = a.s_aux + (long long)bh * a.saux_bh_stride + (long long)s * a.saux_seg_stride;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int col = col0 + wave * 16 * NCT + ct * 16 + lr;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sx[(long long)(16 * it + 4 * lg + j) * DK + col] = st[it][NCT + ct][j];
-            }
+    const bool died = PROBE && died_at >= 0;
+    if (PROBE && tid == 0)
+        a.z_out[((long long)bh * (a.n_seg_total - 1) + (s - 1)) * a.n_vs + vs] = died ? died_at : -1;
+    // destination: s_out (when this segment's state is wanted), s_head for segment 0, s_tail for
+    // the last segment; a cut unit has no final state of its own, except the last segment, whose
+    // final state is then its increment, copied from s_tail
+    float* so = (a.s_out && (a.out_seg < 0 || a.out_seg == s))
+                    ? a.s_out + (long long)bh * a.sout_bh_stride + (long long)s * a.sout_seg_stride
+                    : nullptr;
+    const float* from = nullptr;
+    if (s == 0 && a.s_head) so = a.s_head + (long long)bh * a.shead_bh_stride;
+    if (s == a.tail_seg) {
+        float* tail = a.s_tail ? a.s_tail + (long long)bh * a.stail_bh_stride : nullptr;
+        if (!a.z_limit) so = tail;
+        else if (cut) from = tail;
     }
-    if (a.s_out && (a.out_seg < 0 || a.out_seg == s)) {
-        float* so = a.s_out + (long long)bh * a.sout_bh_stride + (long long)s * a.sout_seg_stride;
+    if (cut && !from) so = nullptr;
+    // element (it, j) of column tile ct of this lane
+    auto elem = [&](int it, int ct, int j) {
+        return (long long)(16 * it + 4 * lg + j) * DK + col0 + wave * 16 * NCT + ct * 16 + lr;
+    };
+    if constexpr (DUAL) {
+        // the transition (none is kept for the last segment); a transition that died is stored as
+        // zeros, and the unit's increment is then formed by the zero-start pass instead
+        if (s != a.tail_seg) {
+            float* sx = a.s_aux + (long long)bh * a.saux_bh_stride + (long long)s * a.saux_seg_stride;
+#pragma unroll
+            for (int it = 0; it < NIT; ++it)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sx[elem(it, ct, j)] = died ? 0.0f : st[it][NCT + ct][j];
+        }
+        if (died) so = nullptr;
+    } else if (died) {
+        if (so) {   // a transition pass: its transition is stored as zeros
+#pragma unroll
+            for (int it = 0; it < NIT; ++it)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) so[elem(it, ct, j)] = 0.0f;
+        }
+        so = nullptr;
+    }
+    if (so && from) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int col = col0 + wave * 16 * NCT + ct * 16 + lr;
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) so[(long long)(16 * it + 4 * lg + j) * DK + col] = st[it][ct][j];
-            }
+                for (int j = 0; j < 4; ++j) so[elem(it, ct, j)] = from[elem(it, ct, j)];
+    } else if (so) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) so[elem(it, ct, j)] = st[it][ct][j];
     }
 }
 
+// The dual pass always stops early (PROBE); a plain pass stops early when a.probe is set, which
+// only the split's transition pass of 4-wave shapes asks for.
 template <class Cfg, bool DUAL = false, bool GATE = false>
 hipError_t launch_prefill_cfg(const PrefillArgs& a, hipStream_t stream) {
     const long long groups = ((long long)a.n_units + 7) / 8;
     const long long nblk = groups * 8 * a.n_vs;
     if (nblk <= 0) return hipSuccess;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((kda_prefill_kernel<Cfg, DUAL, GATE>), dim3((unsigned)nblk), dim3(Cfg::NTH), 0, stream, a);
+    if (a.probe && (!a.z_out || a.seg0 < 1)) return hipErrorInvalidValue;
+    if constexpr (DUAL) {
+        if (!a.probe) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((kda_prefill_kernel<Cfg, true, GATE, true>), dim3((unsigned)nblk), dim3(Cfg::NTH), 0, stream, a);
+    } else if (!a.probe) {
+        hipLaunchKernelGGL((kda_prefill_kernel<Cfg, false, GATE, false>), dim3((unsigned)nblk), dim3(Cfg::NTH), 0, stream, a);
+    } else {
+        if constexpr (Cfg::NW == 4)
+            hipLaunchKernelGGL((kda_prefill_kernel<Cfg, false, GATE, true>), dim3((unsigned)nblk), dim3(Cfg::NTH), 0, stream, a);
+        else
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -119,6 +119,7 @@ struct PipeUnit {
     int b, h, s, bh;
     long long t_begin, t_end;
     int nchunks;
+    bool cut;              // the sequence split's limit ran fewer chunks than the segment holds
     long long HD;          // token stride of every [B, T, H, d] tensor
     long long base_tok;    // element offset of (b, token 0, h, 0)
 };
@@ -537,7 +538,7 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
         return pinned_u((uint32_t)(((16 * it + 4 * lg + j) * DK + colw + 16 * ct + lr) * 4));
     };
     f32x4_t st[NIT][NCT];
-    if (a.init_mode == 1) {
+    if (a.init_mode == 1 || (a.init_mode == 3 && u.s == 0)) {
         const float* sin = a.s_in + (long long)u.bh * a.sin_bh_stride + (long long)u.s * a.sin_seg_stride;
 #pragma unroll
         for (int it = 0; it < NIT; ++it)
@@ -780,15 +781,28 @@ __device__ __forceinline__ void pipe_state_waves(const PrefillArgs& a, const Pip
         if (c + 1 < u.nchunks) x_rhs();
     }
 
-    if (a.s_out && (a.out_seg < 0 || a.out_seg == u.s)) {
-        float* so = a.s_out + (long long)u.bh * a.sout_bh_stride + (long long)u.s * a.sout_seg_stride;
+    // destination: s_out (when this segment's state is wanted), s_head for segment 0, s_tail for
+    // the last segment; a cut unit has no final state of its own, except the last segment, whose
+    // final state is then its increment, copied from s_tail
+    float* so = (a.s_out && (a.out_seg < 0 || a.out_seg == u.s))
+                    ? a.s_out + (long long)u.bh * a.sout_bh_stride + (long long)u.s * a.sout_seg_stride
+                    : nullptr;
+    const float* from = nullptr;
+    if (u.s == 0 && a.s_head) so = a.s_head + (long long)u.bh * a.shead_bh_stride;
+    if (u.s == a.tail_seg) {
+        float* tail = a.s_tail ? a.s_tail + (long long)u.bh * a.stail_bh_stride : nullptr;
+        if (!a.z_limit) so = tail;
+        else if (u.cut) from = tail;
+    }
+    if (u.cut && !from) so = nullptr;
+    if (so) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    *at_byte(so, st_off(it, ct, j)) = st[it][ct][j];
+                    *at_byte(so, st_off(it, ct, j)) = from ? *at_byte(from, st_off(it, ct, j)) : st[it][ct][j];
     }
 }
 
@@ -816,6 +830,17 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void kda_prefill_pipe_kernel(const 
     u.t_end = t_next < a.T ? t_next : a.T;
     const long long ntok = u.t_end - u.t_begin;
     u.nchunks = ntok > 0 ? (int)((ntok + C - 1) / C) : 0;
+    u.cut = false;
+    // sequence split: skip a unit whose increment the transition pass already formed, or run only
+    // the chunks over which the entry state still matters (unit-uniform, before any barrier)
+    if (u.s > 0 && (a.z_gate || a.z_limit)) {
+        const int z = split_count(a.z_in, a.n_seg_total, a.n_vs, u.bh, u.s);
+        if (a.z_gate && z < 0) return;
+        if (a.z_limit && z >= 0 && z < u.nchunks) {
+            u.nchunks = z;
+            u.cut = true;
+        }
+    }
     u.HD = (long long)a.H * DK;
     u.base_tok = (long long)u.b * a.T * u.HD + (long long)u.h * DK;
 

@@ -14,6 +14,9 @@
 // thread holds one row of the step's transition in registers (the next step's
 // row is requested before the current step's products).  fp32 throughout, with
 // each entry summed over m in order (the same sums as one row-by-row product).
+// A step whose transition died out (the transition pass stored it as zeros and
+// recorded a chunk count) is S_in(s+1) = H_s: its transition is neither read nor
+// multiplied, which gives the same bits.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -57,12 +60,19 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(const ScanArgs a) {
     // row `row` of M_s and this thread's columns of H_s, for the step being computed and the next
     auto mrow_of = [&](int s) { return a.M + ((long long)bh * (a.n_seg - 1) + s) * SS + (long long)row * DK; };
     auto hrow_of = [&](int s) { return a.Hinc + ((long long)bh * (a.n_seg - 1) + s) * SS + (long long)row * DK + c0; };
+    // a step whose transition died (the transition pass stored it as zeros) adds nothing to H_s:
+    // its rows are not read and its product is skipped (workgroup-uniform)
+    auto dead = [&](int s) { return a.z != nullptr && split_count(a.z, a.n_seg, a.n_vs, bh, s) >= 0; };
     f32x4_t mr[DK / 4], hr[NQ];
+    bool dead_cur = false;
     if (a.s_first + 1 < a.n_seg) {
+        dead_cur = dead(a.s_first);
         const float* M = mrow_of(a.s_first);
         const float* Hs = hrow_of(a.s_first);
+        if (!dead_cur) {
 #pragma unroll
-        for (int m = 0; m < DK / 4; ++m) mr[m] = *reinterpret_cast<const f32x4_t*>(M + 4 * m);
+            for (int m = 0; m < DK / 4; ++m) mr[m] = *reinterpret_cast<const f32x4_t*>(M + 4 * m);
+        }
 #pragma unroll
         for (int q = 0; q < NQ; ++q) hr[q] = *reinterpret_cast<const f32x4_t*>(Hs + 4 * q);
     }
@@ -74,17 +84,21 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(const ScanArgs a) {
         // next step's operands requested before this step's products
         f32x4_t mn[DK / 4], hn[NQ];
         const bool more = s + 2 < a.n_seg;
+        const bool dead_next = more && dead(s + 1);
         if (more) {
             const float* M = mrow_of(s + 1);
             const float* Hs = hrow_of(s + 1);
+            if (!dead_next) {
 #pragma unroll
-            for (int m = 0; m < DK / 4; ++m) mn[m] = *reinterpret_cast<const f32x4_t*>(M + 4 * m);
+                for (int m = 0; m < DK / 4; ++m) mn[m] = *reinterpret_cast<const f32x4_t*>(M + 4 * m);
+            }
 #pragma unroll
             for (int q = 0; q < NQ; ++q) hn[q] = *reinterpret_cast<const f32x4_t*>(Hs + 4 * q);
         }
         f32x4_t acc[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) acc[q] = hr[q];
+        if (!dead_cur) {
 #pragma unroll
         for (int m = 0; m < DK / 4; ++m) {
 #pragma unroll
@@ -98,6 +112,7 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(const ScanArgs a) {
                 }
             }
         }
+        }
         float* dst = sin + (long long)(s + 1) * SS + (long long)row * DK + c0;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -109,6 +124,7 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(const ScanArgs a) {
             for (int m = 0; m < DK / 4; ++m) mr[m] = mn[m];
 #pragma unroll
             for (int q = 0; q < NQ; ++q) hr[q] = hn[q];
+            dead_cur = dead_next;
         }
     }
 }

@@ -69,10 +69,10 @@ const char *kda_status_string(kda_status_t status);
 
 /*
  * Sequence-split plan that kda_chunk_prefill picks for a shape (the automatic
- * scheduler): `seg_len` tokens per segment after the first (== T when the
- * sequence is not split; the first segment holds the remaining tokens and is
- * the longest, since it runs from S0 while the transitions of the middle
- * segments are formed) and `n_vs` state-column slices per head.  Pages: "Kimi
+ * scheduler): `seg_len` tokens per segment (== T when the sequence is not split;
+ * segments of equal length, the last one possibly shorter, few enough that all
+ * of them run at once on fewer workgroups than the GPU has compute units) and
+ * `n_vs` state-column slices per head.  Pages: "Kimi
  * K3", "Parallelizing Sequential State Updates" (a scheduler spreads
  * long-context prefill over the compute units of one card).  Any output
  * pointer may be NULL.
@@ -82,9 +82,9 @@ kda_status_t kda_chunk_prefill_plan(int B, int T, int H, int dk, int dv, int chu
 
 /*
  * Bytes of device workspace that kda_chunk_prefill needs (the automatic plan):
- * the per-segment transitions and increments and the segments' entry states of
- * a sequence split, 0 when the sequence is not split.  Returns 0 for shapes
- * that kda_chunk_prefill would reject.
+ * the per-segment transitions and increments, the segments' entry states and
+ * the transition pass's chunk counts of a sequence split, 0 when the sequence
+ * is not split.  Returns 0 for shapes that kda_chunk_prefill would reject.
  */
 size_t kda_chunk_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
                                          kda_dtype_t dtype);
@@ -132,18 +132,25 @@ kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v,
  * positive multiple of `chunk`, all segments equal but the last; 0 = automatic;
  * >= T = no split) and `n_vs` state-column slices (1 or 2 for dv = 128, 1 for
  * dv = 64; 0 = automatic).  With a split, segment 0 runs from S0 with its
- * outputs while the transitions M_s (the recurrence applied to the identity
- * with zero values) and increments H_s (from a zero state) of segments
- * 1 .. n-2 are formed; an on-device prefix scan S_in(s+1) = M_s S_in(s) + H_s
- * from segment 0's final state gives every later entry state, and segments
- * 1 .. n-1 then run from them.  Segment 0 runs on a second stream of the
- * library (created once per device, default priority) joined back to `stream`
- * by events (fork after the work already on `stream`, join before the scan); the
- * call stays asynchronous.  Calls from several host threads are serialised
- * while they enqueue a split.
+ * outputs; the transitions M_s of the later segments (the recurrence applied to
+ * the identity with zero values) are formed only until every entry has fallen
+ * below 2^-126, and are then stored as zeros; segments 1 .. n-1 run with their
+ * outputs from a zero state, which gives the increments H_s; an on-device
+ * prefix scan S_in(s+1) = M_s S_in(s) + H_s from segment 0's final state gives
+ * every later entry state; and each segment reruns from its entry state only
+ * the chunks before its transition died, overwriting those outputs (all of
+ * them where the transition never dies, e.g. with no decay and beta = 0).  Past
+ * that point an entry state adds less than dk * 2^-126 times its own size to
+ * the state, so the results are those of one pass up to rounding.  Segment 0
+ * runs on a second stream of the library (created once per device, default
+ * priority) joined back to `stream` by events (fork after the work already on
+ * `stream`, join before the scan); the call stays asynchronous.  Calls from
+ * several host threads are serialised while they enqueue a split.
  * Pages: "Kimi K3's architecture", "The bill comes due in the serving stack"
  * (per segment, the transition and the state reached from zero combine
- * exactly across segments).
+ * exactly across segments); "Inside Kimi K3" (academa.ai lecture), sequence
+ * paragraph (the diagonal gate scales down what the state keeps from earlier
+ * tokens).
  * The workspace must hold kda_chunk_prefill_workspace_bytes_ex(..., seg_len).
  */
 kda_status_t kda_chunk_prefill_ex(const void *q, const void *k, const void *v,
@@ -273,7 +280,7 @@ kda_status_t kda_spec_commit(const void *q, const void *k, const void *v,
  * other allocating routine.  A sequence split takes its transitions, increments
  * and entry states from a fixed device array of KDA_NOALLOC_SCRATCH_BYTES bytes
  * inside the library, and every one of its launches runs on `stream` (segment 0
- * and the transition/increment pass one after the other, not side by side).
+ * inside the zero-start launch of the other segments, not on a second stream).
  *
  *   arguments as for kda_chunk_prefill_ex, without workspace / workspace_bytes
  *   returns KDA_ERR_WORKSPACE when kda_chunk_prefill_workspace_bytes_ex(..., seg_len)

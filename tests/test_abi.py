@@ -136,10 +136,19 @@ def test_prefill_overlaps(lib, host_only):
     assert _prefill(lib, S0=_ptrs(6), S_T=args["v"], **args) == INVALID   # S_T over an input
 
 
+def _split_workspace(bh, n, dk, dv):
+    """Bytes of a split's workspace over n segments: transitions and increments of segments
+    1 .. n-1 (n - 1 slots each), entry states (n slots), then the transition pass's chunk counts
+    (two int32 per (b, h) and segment after the first), padded to 16 bytes."""
+    mats = (n - 1) * (dk * dk + dk * dv) + n * dk * dv
+    counts = (bh * (n - 1) * 2 * 4 + 15) // 16 * 16
+    return bh * mats * 4 + counts
+
+
 def test_prefill_workspace_required(lib, host_only):
     args = _ok_ptrs()
     need = lib.kda_chunk_prefill_workspace_bytes_ex(1, 8192, 2, 128, 128, 64, BF16, 2048)
-    assert need == 2 * (3 * 2 * 128 * 128 + 4 * 128 * 128) * 4
+    assert need == _split_workspace(2, 4, 128, 128)
     assert _prefill(lib, T=8192, seg=2048, **args) == WORKSPACE
     assert _prefill(lib, T=8192, seg=2048, ws=_ptrs(7), ws_bytes=need - 4, **args) == WORKSPACE
 
@@ -194,12 +203,12 @@ def test_plan_rules(lib):
 
 
 def test_automatic_plan_properties(lib):
-    """Over a sweep of shapes the automatic plan keeps its rules: segments are whole chunks that
-    cover the sequence; a split has at least 3 segments, each phase of it fits in fewer workgroups
-    than the 256 compute units (units * (n - 1) <= 255), its segments are not much shorter than
-    max(512, 8 sqrt(T)) and the first takes what the others leave (at most about twice their
-    length); shapes that already fill the chip, or are too short, are not split.  The
-    workspace matches the plan (transition + increment per segment but the last, entry states)."""
+    """Over a sweep of shapes the automatic plan keeps its rules: segments are whole chunks of
+    equal length (the last one possibly shorter) that cover the sequence; a split has at least 3
+    segments, its widest step (every segment at once) fits in fewer workgroups than the 256
+    compute units (units * n <= 255), and its segments are not shorter than max(512, 8 sqrt(T));
+    shapes that already fill the chip, or are too short, are not split.  The workspace matches
+    the plan."""
     import itertools
     import math
     seg = ctypes.c_int(0)
@@ -217,16 +226,14 @@ def test_automatic_plan_properties(lib):
         lmin = max(512, 8 * math.sqrt(T))
         if L >= T:   # no split
             assert ws == 0
-            assert 2 * units > 255 or T < 3 * lmin or (255 // units) < 2, (B, H, T, d, dt, chunk)
+            assert 2 * units > 256 or T < 3 * lmin or min(255 // units, int(T // lmin)) < 3, \
+                (B, H, T, d, dt, chunk)
             continue
-        per = B * H * d * d * 4
-        assert ws % per == 0 and (ws // per + 2) % 3 == 0, (B, H, T, d, dt, chunk, ws)
-        n = (ws // per + 2) // 3
-        assert L % chunk == 0 and L >= 0.5 * lmin, (B, H, T, d, dt, chunk, L)
-        assert n >= 3 and units * (n - 1) <= 255, (B, H, T, d, dt, chunk, n)
-        # segment 0 takes what the others leave: more than nothing, at most about the cost ratio
-        # of the two passes (<= 2) times L, plus half a chunk of rounding per segment
-        assert 0 < T - (n - 1) * L <= 2 * L + n * chunk, (B, H, T, d, dt, chunk, n, L)
+        n = -(-T // L)
+        assert ws == _split_workspace(B * H, n, d, d), (B, H, T, d, dt, chunk, ws)
+        assert L % chunk == 0 and L >= lmin - chunk, (B, H, T, d, dt, chunk, L)
+        assert n >= 3 and units * n <= 255, (B, H, T, d, dt, chunk, n)
+        assert 0 < T - (n - 1) * L <= L, (B, H, T, d, dt, chunk, n, L)
         checked += 1
     assert checked > 20   # the sweep does reach the split branch
 
@@ -317,7 +324,7 @@ def test_fp32_chunk64_is_supported(lib):
         assert seg.value % 64 == 0 and seg.value < (1 << 16)
         assert lib.kda_chunk_prefill_workspace_bytes(1, 1 << 16, 2, d, d, 64, F32) > 0
         assert lib.kda_chunk_prefill_workspace_bytes_ex(1, 4096, 2, d, d, 64, F32, 1024) == \
-            2 * (3 * 2 * d * d + 4 * d * d) * 4
+            _split_workspace(2, 4, d, d)
     args = _ok_ptrs()
     assert _prefill(lib, dt=F32, chunk=64, seg=96, **args) == INVALID   # not a multiple of 64
 

@@ -21,19 +21,22 @@ def _kda():
     return kda
 
 
-@pytest.mark.parametrize("dtype,d,T,chunk,every,seg", [
-    ("bf16", 128, 1000, 64, 128, 0),       # 7 checkpoints, ragged tail, no split
-    ("bf16", 128, 1000, 64, 128, 256),     # the same through the sequence split
-    ("bf16", 64, 640, 32, 64, 0),
-    ("f32", 64, 300, 16, 32, 0),
-    ("bf16", 128, 512, 64, 512, 0),        # one checkpoint, at the last token
-    ("bf16", 128, 12288, 64, 4096, 0),     # automatic split: segments 4480 + 3904 + 3904 tokens
-    ("f32", 128, 700, 64, 128, 0),         # fp32 with 64-token chunks
+@pytest.mark.parametrize("dtype,d,T,chunk,every,seg,decay", [
+    ("bf16", 128, 1000, 64, 128, 0, "slow"),       # 7 checkpoints, ragged tail, no split
+    ("bf16", 128, 1000, 64, 128, 256, "slow"),     # the same through the sequence split
+    ("bf16", 128, 1024, 64, 128, 256, "sig2"),     # split whose transitions die within a segment
+    ("bf16", 128, 1000, 64, 64, 192, "sig2"),      # ... checkpoints inside the rerun chunks too
+    ("f32", 64, 1000, 32, 64, 256, "sig2"),        # ... on the 4-wave transition pass
+    ("bf16", 64, 640, 32, 64, 0, "slow"),
+    ("f32", 64, 300, 16, 32, 0, "slow"),
+    ("bf16", 128, 512, 64, 512, 0, "slow"),        # one checkpoint, at the last token
+    ("bf16", 128, 12288, 64, 4096, 0, "slow"),     # automatic split: 13 segments of 960 tokens
+    ("f32", 128, 700, 64, 128, 0, "slow"),         # fp32 with 64-token chunks
 ])
-def test_prefill_checkpoints_match_oracle(dtype, d, T, chunk, every, seg):
+def test_prefill_checkpoints_match_oracle(dtype, d, T, chunk, every, seg, decay):
     kda = _kda()
-    print(f"ckpt dtype={dtype} d={d} T={T} chunk={chunk} every={every} seg={seg}", flush=True)
-    inp = gen.make_prefill_inputs(2, T, 2, d, d, dtype, "slow", 1.0, 90 + T, 0.0, "cpu")
+    print(f"ckpt dtype={dtype} d={d} T={T} chunk={chunk} every={every} seg={seg} decay={decay}", flush=True)
+    inp = gen.make_prefill_inputs(2, T, 2, d, d, dtype, decay, 1.0, 90 + T, 0.0, "cpu")
     dd = to_device(inp)
     ck0 = torch.full((2, T // every, 2, d, d), float("nan"), dtype=torch.float32, device="cuda")
     o, st, ck = kda.chunk_prefill_ckpt(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], dd["S0"],

@@ -20,6 +20,7 @@ def _kda():
 
 
 @pytest.mark.parametrize("B,T,chunk,seg,decay", [(2, 700, 64, 0, "sig2"), (2, 1000, 64, 256, "slow"),
+                                                 (2, 1000, 64, 256, "sig2"),   # split, transitions die
                                                  (2, 333, 32, 0, "sig2"), (2, 200, 16, 0, "sig2"),
                                                  (1, 12288, 64, 0, "slow")])   # automatic split
 def test_prefill_gate_matches_oracle(B, T, chunk, seg, decay):

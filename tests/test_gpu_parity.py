@@ -184,16 +184,13 @@ def test_prefill_sequence_split_matches_oracle(dtype, chunk, seg):
 
 @pytest.mark.parametrize("T,H", [(12288, 1), (13000, 1), (4096, 8)])
 def test_prefill_automatic_split(T, H):
-    """The automatic plan splits a sequence of a few thousand tokens over few heads; segment 0
-    (run from S0 beside the transition/increment pass of the middle segments) is at least as
-    long as the others (12288 and 13000 tokens: longer; 13000: ragged last segment)."""
+    """The automatic plan splits a sequence of a few thousand tokens over few heads into segments
+    of equal length, the last one possibly shorter (13000 tokens: ragged)."""
     kda = _kda()
     seg, nvs = kda.prefill_plan(1, T, H, 128, 128, 64)
     assert nvs == 1 and seg < T and seg % 64 == 0
-    # workspace: transitions and increments of n - 1 segments plus n entry states
-    per_state = H * 128 * 128 * 4
-    n_seg = (kda.prefill_workspace_bytes(1, T, H, 128, 128, 64) // per_state + 2) // 3
-    assert n_seg >= 3 and T - (n_seg - 1) * seg >= seg   # the first segment holds the surplus
+    n_seg = -(-T // seg)
+    assert n_seg >= 3 and 0 < T - (n_seg - 1) * seg <= seg
     inp = _case(1, T, H, 128, "bf16", decay="slow", s0=1.0, seed=31)
     o, st = _run_prefill(inp, 64)
     o_ref, s_ref = _oracle(inp)
