@@ -235,6 +235,8 @@ kda_status_t resolve_plan(int B, int T, int H, int dk, int dv, int chunk, kda_dt
     }
     const long long ns = T > 0 ? segment_count(T, sl, sh) : 1;
     if (ns > (1 << 20)) return KDA_ERR_UNSUPPORTED;
+    // every launch of a split counts its units (b, h, segment, slice) in an int
+    if ((long long)B * H * ns * vs > (1LL << 30)) return KDA_ERR_UNSUPPORTED;
     *seg_len = sl;
     *n_seg = (int)ns;
     *n_vs = vs;

@@ -153,6 +153,20 @@ def test_prefill_workspace_required(lib, host_only):
     assert _prefill(lib, T=8192, seg=2048, ws=_ptrs(7), ws_bytes=need - 4, **args) == WORKSPACE
 
 
+def test_split_unit_count_limit(lib, host_only):
+    """A split whose launches would count more than 2^30 units (b, h, segment, slice) is refused
+    before anything is enqueued: 2^11 sequences x 2^16 heads (the most B * H allows) in 16
+    segments of 64 tokens.  The same shape unsplit is a valid plan."""
+    seg = ctypes.c_int(0)
+    nvs = ctypes.c_int(0)
+    B, H = 1 << 11, 1 << 16
+    assert lib.kda_chunk_prefill_workspace_bytes_ex(B, 1024, H, 64, 64, 64, BF16, 64) == 0
+    assert _prefill(lib, B=B, T=1024, H=H, dk=64, dv=64, seg=64) == UNSUPPORTED
+    assert lib.kda_chunk_prefill_plan(B, 1024, H, 64, 64, 64, BF16, ctypes.byref(seg),
+                                      ctypes.byref(nvs)) == OK
+    assert seg.value == 1024
+
+
 def test_prefill_empty_batch_is_noop(lib):
     assert _prefill(lib, B=0, q=None, k=None, v=None, la=None, beta=None, o=None) == OK
     assert _prefill(lib, H=0, q=None, k=None, v=None, la=None, beta=None, o=None) == OK
