@@ -391,7 +391,7 @@ namespace {
 
 // Every prefill entry point: the decay input is log_alpha (fp32) or, with gmode, gate (bf16 raw
 // gate pre-activation).  side_ok = false keeps a sequence split entirely on `stream` (segment 0
-// then the transition/increment pass, one after the other; no stream or event of the library's).
+// inside the zero-start launch of the other segments; no stream or event of the library's).
 kda_status_t prefill_entry(const void* q, const void* k, const void* v, const float* log_alpha, const void* gate,
                            bool gmode, const float* beta, const float* S0, void* o, float* S_T, int B, int T, int H, int dk,
                            int dv, int chunk, kda_dtype_t dt, int ckpt_every, float* S_ckpt, int seg_len,

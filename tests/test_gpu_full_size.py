@@ -71,12 +71,12 @@ def test_model_width_prefill_all_heads():
 
 
 def test_long_context_all_heads_both_plans():
-    """The workload's 64K-token segments and the library's own plan (segment 0 longer, run from
-    S0 beside the transition/increment pass of the middle segments), every head."""
+    """The workload's 64K-token segments and the library's own plan (equal segments, all of them
+    running at once), every head."""
     kda = _kda()
     w = gen.WORKLOADS["long_1m"]
     auto_seg, _ = kda.prefill_plan(w.B, w.T, w.H, w.dk, w.dv, w.chunk)
-    print(f"long context: {w.note}; automatic plan: segments of {auto_seg} after the first", flush=True)
+    print(f"long context: {w.note}; automatic plan: segments of {auto_seg}", flush=True)
     d = gen.workload_inputs(w, device="cuda")
     runs = []
     for seg in (w.segment, 0):

@@ -173,8 +173,9 @@ def test_prefill_mixed_bound_tokens():
                                              ("bf16", 64, 512), ("bf16", 64, 384), ("f32", 32, 512),
                                              ("f32", 64, 256)])
 def test_prefill_sequence_split_matches_oracle(dtype, chunk, seg):
-    """Segment 0 from S0 beside the transitions + increments of the middle segments, prefix scan,
-    rerun from entry states.  T = 1000 gives 2 to 8 segments (2: no transition pass, no scan)."""
+    """Segment 0 from S0 beside the transition pass and the zero-start runs of the later
+    segments, prefix scan, rerun from entry states.  T = 1000 gives 2 to 8 segments (2: no
+    scan); slow decay keeps every transition alive, so this is the full two-pass split."""
     inp = _case(2, 1000, 2, 128 if dtype == "bf16" else 64, dtype, decay="slow", s0=1.0, seed=24)
     o, st = _run_prefill(inp, chunk, seg_len=seg)
     o_ref, s_ref = _oracle(inp)
@@ -246,9 +247,9 @@ def test_prefill_column_split_matches_unsplit():
 
 
 def test_prefill_split_one_pass_matches_two_pass():
-    """With one column slice the transitions and increments come from one shared pass; with two
-    slices from two separate passes.  Both match the oracle and each other to the bf16
-    tolerance (the shared pass may run a different chunk length)."""
+    """With one column slice the transitions come from a pass shared with the increments; with
+    two slices from a transition pass of their own, the increments from the zero-start pass.
+    Both match the oracle and each other to the bf16 tolerance."""
     inp = _case(1, 900, 2, 128, "bf16", decay="slow", s0=1.0, seed=29)
     o1, s1 = _run_prefill(inp, 64, seg_len=192, n_vs=1)
     o2, s2 = _run_prefill(inp, 64, seg_len=192, n_vs=2)
