@@ -247,7 +247,7 @@ kda_status_t resolve_plan(int B, int T, int H, int dk, int dv, int chunk, kda_dt
 // Split workspace: transitions M [B*H, n_seg-1, dk, dk] (slot s for segment s; slot 0 unused),
 // increments H [B*H, n_seg-1, dk, dv] (likewise), entry states S_in [B*H, n_seg, dk, dv] (slot s
 // for segment s >= 1; slot 0 holds the last segment's increment), then the transition pass's
-// chunk counts [B*H, n_seg-1, 2] int32 (room for two column slices), padded to 16 bytes.
+// chunk counts [B*H, n_seg-1, n_vs] int32 in a region sized for two column slices, padded to 16 bytes.
 size_t workspace_for(int B, int H, int dk, int dv, int n_seg) {
     if (n_seg <= 1) return 0;
     const size_t bh = (size_t)B * H;

@@ -106,3 +106,39 @@ def test_split_short_cut_is_deterministic_and_matches_no_alloc():
                               seg_len=512, o=o3, S_T=st3)
     torch.cuda.synchronize()
     assert torch.equal(o1, o3) and torch.equal(st1, st3)
+
+
+def test_split_transition_pass_stops_where_transitions_die():
+    """The mechanism itself, read back from the caller's workspace (the transition pass's chunk
+    counts follow the transitions, increments and entry states: int32 [B*H, n_seg - 1, n_vs] in a
+    region sized for two slices).  Fast decay: every count is a few chunks.  An identity head
+    (log alpha = 0, beta = 0): -1, never died, so the full two-pass split ran there.  A head
+    that is the identity for its first 600 tokens: -1 in the segment that lies inside that
+    range, a few chunks past token 600 in the segment holding it, a few chunks after that."""
+    kda = _kda()
+    B, T, H, d, seg = 2, 1000, 2, 128, 256
+    ns = -(-T // seg)
+    for pattern in ("mixed", "late"):
+        inp = _inputs("bf16", d, T, pattern, seed=91)
+        dd = to_device(inp)
+        need = kda.prefill_workspace_bytes(B, T, H, d, d, 64, seg_len=seg)
+        ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")
+        kda.chunk_prefill(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"], dd["S0"], chunk=64,
+                          seg_len=seg, workspace=ws)
+        torch.cuda.synchronize()
+        SS = d * d * 4
+        off = B * H * ((ns - 1) * 2 + ns) * SS
+        z = ws[off:off + B * H * (ns - 1) * 4].view(torch.int32).view(B, H, ns - 1).cpu()
+        print(f"{pattern}: chunk counts of segments 1..{ns - 1} per (b, h):\n{z}", flush=True)
+        if pattern == "mixed":
+            assert ((z[:, 0] >= 1) & (z[:, 0] <= 3)).all()   # fast decay: dead within a few chunks
+            assert (z[:, 1] == -1).all()                     # identity head: never dies
+        else:
+            # head 0: segment 1 = tokens 256..511 lies inside the identity range; segment 2 =
+            # tokens 512..767 holds token 600 (chunk 1 of the segment); segment 3 decays at once
+            assert (z[:, 0, 0] == -1).all()
+            assert ((z[:, 0, 1] >= 2) & (z[:, 0, 1] <= 4)).all()
+            assert ((z[:, 0, 2] >= 1) & (z[:, 0, 2] <= 3)).all()
+            # head 1: the first 100 tokens of every segment are the identity (chunk 1 holds token
+            # 100), then fast decay
+            assert ((z[:, 1] >= 2) & (z[:, 1] <= 4)).all()
