@@ -544,6 +544,7 @@ def main():
         result["prefill_fused_gate"] = bench_prefill_gate(kda, gen, w, d, args.steps, args.warmup)
     if not args.prefill_only and not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sampled_vs_oracle"] = cpu_baseline(d, w, o_dev)
+        result["cpu_baseline"]["gpu_speedup"] = tok_s / result["cpu_baseline"]["value"]
     del d, o_dev
     torch.cuda.empty_cache()
 
@@ -560,6 +561,8 @@ def main():
                             "tokens_per_s": wd.N * args.decode_steps / dwall}
         if not args.no_cpu_baseline:
             result["decode"]["cpu_baseline"] = cpu_baseline_decode(gen)
+            result["decode"]["cpu_baseline"]["gpu_speedup"] = (result["decode"]["tokens_per_s"] /
+                                                               result["decode"]["cpu_baseline"]["value"])
     if not args.prefill_only and not args.no_spec:
         result["spec_decode"] = bench_spec(kda, gen)
     if not args.prefill_only and not args.no_long:
@@ -580,6 +583,8 @@ def main():
                                                      "frac_of_hbm_peak": one_pass * nsteps / awall / (HBM_PEAK_GBS * 1e9)}}
         if not args.no_cpu_baseline:
             result["long_context"]["cpu_baseline"] = cpu_baseline_long(gen)
+            result["long_context"]["cpu_baseline"]["gpu_speedup"] = (result["long_context"]["tokens_per_s"] /
+                                                                     result["long_context"]["cpu_baseline"]["value"])
     if not args.prefill_only:
         peaks = measure_peaks()
         rf = result["roofline"]
