@@ -6,6 +6,9 @@ accumulated in float64 over the whole tensor (no float64 copy of a whole output 
   (sequence, head) pairs, every output and every final state;
 * 1M-token context: B=1, H=16, T=1,048,576: the workload's 64K-token segments and the automatic
   plan, all 16 heads, every output and final state;
+* model width with the fused gate (bf16 raw pre-activation in place of log alpha) and with state
+  checkpoints every 4096 tokens, as the benchmark times them: all 224 pairs, every output, final
+  state and checkpoint;
 * decode: 256 sequences x 56 heads, 1000 consecutive steps from S ~ N(0, 0.02^2): every output of
   every step and the final states of 32 seeded sequences x all 56 heads (1792 states; the
   other sequences must stay finite).  A decode step is one token of the recurrence, so 1000 steps
@@ -37,16 +40,27 @@ def _heads(d, b, h0, h1):
             None if d["S0"] is None else d["S0"][b:b + 1, h0:h1].contiguous().cpu())
 
 
-def _compare_all_heads(d, outs, group, col_block, label):
-    """Every (b, h) of each (o, S_T) in outs against the oracle, `group` heads per oracle call."""
+def _compare_all_heads(d, outs, group, col_block, label, gate=None, ck=None, every=0):
+    """Every (b, h) of each (o, S_T) in outs against the oracle, `group` heads per oracle call.
+    With `gate`, the oracle takes the raw gate in place of log alpha; with `ck` (checkpoints of
+    the first output pair, [B, T // every, H, d, d]), the checkpoints are compared too."""
     B, T, H, _ = d["q"].shape
     accs = [(Accum(f"{name} o", "bf16"), Accum(f"{name} S_T", "bf16")) for name, _, _ in outs]
+    acc_ck = Accum(f"{label} checkpoints", "bf16") if ck is not None else None
     for b in range(B):
         for h0 in range(0, H, group):
             h1 = min(H, h0 + group)
             print(f"  {label}: oracle on b={b} heads {h0}..{h1 - 1}", flush=True)
             q, k, v, la, bt, s0 = _heads(d, b, h0, h1)
-            o_ref, s_ref = oracle.prefill(q, k, v, la, bt, s0, col_block=col_block)
+            if gate is not None:
+                g = gate[b:b + 1, :, h0:h1].contiguous().cpu()
+                o_ref, s_ref = oracle.prefill_gate(q, k, v, g, bt, s0)
+            elif ck is not None:
+                o_ref, s_ref, ck_ref = oracle.prefill_ckpt(q, k, v, la, bt, s0, every)
+                for h in range(h0, h1):
+                    acc_ck.add(ck[b:b + 1, :, h:h + 1], ck_ref[:, :, h - h0:h - h0 + 1], (b, h))
+            else:
+                o_ref, s_ref = oracle.prefill(q, k, v, la, bt, s0, col_block=col_block)
             for (_, o, st), (ao, ast) in zip(outs, accs):
                 for h in range(h0, h1):
                     ao.add(o[b:b + 1, :, h:h + 1], o_ref[:, :, h - h0:h - h0 + 1], (b, h))
@@ -55,6 +69,8 @@ def _compare_all_heads(d, outs, group, col_block, label):
     for ao, ast in accs:
         ao.check()
         ast.check()
+    if acc_ck is not None:
+        acc_ck.check()
 
 
 def test_model_width_prefill_all_heads():
@@ -68,6 +84,39 @@ def test_model_width_prefill_all_heads():
                       o=o, S_T=st)
     torch.cuda.synchronize()
     _compare_all_heads(d, [("model width", o, st)], group=8, col_block=32, label="model width")
+
+
+def test_model_width_gate_all_heads():
+    """The fused bounded gate at model width, as timed: the gate pre-activations the benchmark
+    draws (bf16, N(0, 2)), every output and final state."""
+    kda = _kda()
+    w = gen.WORKLOADS["model_width"]
+    print(f"model width, fused gate: {w.note}", flush=True)
+    d = gen.workload_inputs(w, device="cuda")
+    g = gen.make_gate(w.B, w.T, w.H, w.dk, w.dtype, seed=w.seed, device="cuda")
+    o = nan_like(d["v"])
+    st = nan_like(d["S0"])
+    kda.chunk_prefill_gate(d["q"], d["k"], d["v"], g, d["beta"], d["S0"], chunk=w.chunk, o=o, S_T=st)
+    torch.cuda.synchronize()
+    _compare_all_heads(d, [("model width, gate", o, st)], group=8, col_block=32, label="gate", gate=g)
+
+
+def test_model_width_checkpoints_all_heads():
+    """State checkpoints every 4096 tokens at model width, as timed: every checkpoint, output and
+    final state."""
+    kda = _kda()
+    w = gen.WORKLOADS["model_width"]
+    every = 4096
+    print(f"model width, checkpoints every {every}: {w.note}", flush=True)
+    d = gen.workload_inputs(w, device="cuda")
+    o = nan_like(d["v"])
+    st = nan_like(d["S0"])
+    ck = torch.full((w.B, w.T // every, w.H, w.dk, w.dv), float("nan"), dtype=torch.float32, device="cuda")
+    kda.chunk_prefill_ckpt(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"], chunk=w.chunk,
+                           ckpt_every=every, o=o, S_T=st, S_ckpt=ck)
+    torch.cuda.synchronize()
+    _compare_all_heads(d, [("model width, checkpoints", o, st)], group=8, col_block=32, label="checkpoints",
+                       ck=ck, every=every)
 
 
 def test_long_context_all_heads_both_plans():
