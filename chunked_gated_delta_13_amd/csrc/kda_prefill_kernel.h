@@ -21,10 +21,10 @@
 //   B   A_ri = beta_r <Lk_r, R_i>, Bqk_ri = <Lq_r, R_i>  one dense MFMA tile per (row tile,
 //       column tile <= row tile), R_i = Kd_i times 2^{rho_row - rho_col} for earlier tiles;
 //       strict / inclusive lower masks by select
-//   C   T = (I + A)^{-1}: forward substitution in the 16x16 diagonal blocks, then
-//       T_ab = -T_aa sum_c A_ac T_cb band by band
+//   C   T_aa = (I + A_aa)^{-1} for the 16x16 diagonal blocks, by forward substitution
 //   D   X = K~ S, P = Q~ S with K~ = Lk 2^{rho_a}, Q~ = Lq 2^{rho_a}
-//       U = T (beta (V - X))
+//       U = (I + A)^{-1} (beta (V - X)) by blocked forward substitution:
+//           U_a = T_aa (RHS_a - sum_{b<a} A_ab U_b)
 //       O = P + Bqk U
 //       S <- Diag(2^{g_C}) S + K'^T U
 // Every product runs on the matrix cores (bf16 operands / fp32 accumulate, or
